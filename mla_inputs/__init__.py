@@ -1,0 +1,271 @@
+"""Seeded synthetic inputs for MLA paged decode.
+
+This module only *makes* inputs: random numbers, their bf16 / fp8-e4m3
+encodings, a paged pool, a block table and the per-request lengths.  It holds
+none of the attention arithmetic, so both the fp64 oracle (``oracle/``) and
+the HIP library (``mla_paged_decode_02_amd``) can consume the same workloads
+without sharing any code that computes a result.
+
+Layouts follow the problem statement of the AITER MLA backend pages:
+
+* ``q``        [T, H, 576]  -- 512 latent (q_nope absorbed) + 64 rope dims.
+* ``kv_cache`` [num_blocks, block_size, 576] -- one latent row per token
+  (first 512 dims are also V).
+* ``block_table`` int32 [num_reqs, max_blocks], ``seq_lens`` int32 [num_reqs],
+  ``qo_indptr`` int32 [num_reqs + 1].
+
+Encodings are returned as raw bits (numpy has no bf16 / fp8 type):
+bf16 -> uint16, fp8-e4m3fn -> uint8.  Float-to-code rounding is done by
+torch's CPU casts (round to nearest even); fp8 values are clamped to +-448
+first so nothing saturates to NaN.
+
+The five named workloads mirror the sizes the pages measure on (bs=52,
+qlen=1, 16384 KV tokens per request) plus a tiny and a ragged case.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+import torch
+
+HEAD_DIM = 576
+KV_LORA_RANK = 512
+ROPE_DIM = HEAD_DIM - KV_LORA_RANK
+FP8_E4M3_MAX = 448.0
+
+# Poison codes written into pages the kernel must never read.
+BF16_NAN_BITS = 0x7FC0
+FP8_E4M3_NAN_BYTE = 0x7F
+
+
+@dataclass
+class Workload:
+    """One decode batch, fully described by host arrays (encoded bits)."""
+
+    name: str
+    num_heads: int
+    block_size: int
+    q_dtype: str  # "bf16" | "fp8_e4m3"
+    kv_dtype: str  # "bf16" | "fp8_e4m3"
+    q: np.ndarray  # [T, H, 576] uint16 (bf16 bits) or uint8 (e4m3 bytes)
+    kv_cache: np.ndarray  # [num_blocks, block_size, 576] uint16 / uint8
+    block_table: np.ndarray  # int32 [num_reqs, max_blocks]
+    seq_lens: np.ndarray  # int32 [num_reqs]
+    qo_indptr: np.ndarray  # int32 [num_reqs + 1]
+    softmax_scale: float
+    causal: bool = False
+    q_scale: Optional[float] = None  # dequant multiplier (None -> 1.0)
+    kv_scale: Optional[float] = None
+    sinks: Optional[np.ndarray] = None  # float32 [H]
+    tile_size: int = 0  # 0 -> largest pow2 divisor of block, capped at 128
+    num_segments: int = 0  # 0 -> library planner decides
+    seed: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_reqs(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_qlen(self) -> int:
+        d = np.diff(self.qo_indptr)
+        return int(d.max()) if d.size else 0
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.seq_lens.size else 0
+
+    def kv_bytes_touched(self) -> int:
+        """Bytes of cache rows the batch must read once (the pages' 1x unit)."""
+        esz = 2 if self.kv_dtype == "bf16" else 1
+        return int(self.seq_lens.astype(np.int64).sum()) * HEAD_DIM * esz
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _encode(x: torch.Tensor, dtype: str) -> tuple[np.ndarray, Optional[float]]:
+    """fp32 values -> (code array, per-tensor dequant scale or None)."""
+    if dtype == "bf16":
+        return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), None
+    if dtype == "fp8_e4m3":
+        amax = float(x.abs().max()) if x.numel() else 1.0
+        scale = amax / FP8_E4M3_MAX if amax > 0 else 1.0
+        y = (x / scale).clamp_(-FP8_E4M3_MAX, FP8_E4M3_MAX)
+        return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), float(np.float32(scale))
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def _poison_code(dtype: str):
+    return BF16_NAN_BITS if dtype == "bf16" else FP8_E4M3_NAN_BYTE
+
+
+def make_workload(
+    *,
+    name: str,
+    seq_lens,
+    num_heads: int,
+    block_size: int,
+    dtype: str = "bf16",
+    qlens=None,
+    causal: bool = False,
+    sinks: bool = False,
+    softmax_scale: float = 1.0 / math.sqrt(192.0),
+    tile_size: int = 0,
+    num_segments: int = 0,
+    seed: int = 0,
+    poison: bool = True,
+    shuffle_pool: bool = True,
+    extra_bt_cols: int = 0,
+    q_scale_override: Optional[float] = None,
+) -> Workload:
+    """Build a paged decode batch.
+
+    * Every request's pages are drawn from one pool through a random
+      permutation (``shuffle_pool``).
+    * With ``poison`` one extra block filled with NaN codes is appended; the
+      unused tail of each request's last page and every block-table entry past
+      the request's last page are pointed at / filled with NaN.  A kernel that
+      reads a row it should not read turns the output into NaN.
+    * ``qlens`` gives the new query tokens per request (default 1).
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    num_reqs = int(seq_lens.shape[0])
+    if qlens is None:
+        qlens = np.ones(num_reqs, dtype=np.int64)
+    qlens = np.asarray(qlens, dtype=np.int64)
+    assert qlens.shape == (num_reqs,)
+    g = _gen(seed)
+
+    pages_per_req = (seq_lens + block_size - 1) // block_size
+    n_pages = int(pages_per_req.sum())
+    max_blocks = max(int(pages_per_req.max()) if num_reqs else 0, 1) + extra_bt_cols
+    num_blocks = n_pages + (1 if poison else 0)
+    poison_block = n_pages  # index of the NaN block when poison=True
+
+    # Values ~N(0,1): KV rows and queries.
+    kv = torch.randn(num_blocks * block_size * HEAD_DIM, generator=g, dtype=torch.float32)
+    kv = kv.view(num_blocks, block_size, HEAD_DIM)
+    T = int(qlens.sum())
+    q = torch.randn(T * num_heads * HEAD_DIM, generator=g, dtype=torch.float32)
+    q = q.view(T, num_heads, HEAD_DIM)
+
+    kv_codes, kv_scale = _encode(kv, dtype)
+    q_codes, q_scale = _encode(q, dtype)
+    if q_scale_override is not None:
+        q_scale = q_scale_override
+    del kv, q
+
+    perm = torch.randperm(n_pages, generator=g).numpy() if shuffle_pool else np.arange(n_pages)
+    fill = poison_block if poison else 0
+    bt = np.full((num_reqs, max_blocks), fill, dtype=np.int32)
+    cursor = 0
+    for r in range(num_reqs):
+        k = int(pages_per_req[r])
+        bt[r, :k] = perm[cursor : cursor + k]
+        cursor += k
+
+    if poison:
+        code = _poison_code(dtype)
+        kv_codes[poison_block] = code
+        for r in range(num_reqs):
+            k = int(pages_per_req[r])
+            tail = int(seq_lens[r]) - (k - 1) * block_size if k else 0
+            if k and tail < block_size:
+                kv_codes[bt[r, k - 1], tail:] = code
+
+    qo = np.zeros(num_reqs + 1, dtype=np.int32)
+    qo[1:] = np.cumsum(qlens)
+
+    sink_arr = None
+    if sinks:
+        sink_arr = torch.randn(num_heads, generator=g, dtype=torch.float32).numpy()
+
+    return Workload(
+        name=name,
+        num_heads=num_heads,
+        block_size=block_size,
+        q_dtype=dtype,
+        kv_dtype=dtype,
+        q=q_codes,
+        kv_cache=kv_codes,
+        block_table=bt,
+        seq_lens=seq_lens.astype(np.int32),
+        qo_indptr=qo,
+        softmax_scale=float(softmax_scale),
+        causal=causal,
+        q_scale=q_scale,
+        kv_scale=kv_scale,
+        sinks=sink_arr,
+        tile_size=tile_size,
+        num_segments=num_segments,
+        seed=seed,
+        meta={"poison_block": poison_block if poison else None},
+    )
+
+
+# ---------------------------------------------------------------------------
+# Named workloads.  Full sizes are those the decode measurements are quoted
+# on (bs=52, qlen=1, 16384 KV tokens per request); ``scale`` < 1 shrinks the
+# batch and context so the fp64 oracle finishes in seconds.
+# ---------------------------------------------------------------------------
+
+def tiny() -> Workload:
+    """2 requests, lengths {100, 257}, 16 heads, bf16, page = TILE = 16, S = 4."""
+    return make_workload(name="tiny", seq_lens=[100, 257], num_heads=16, block_size=16,
+                         dtype="bf16", num_segments=4, seed=1, extra_bt_cols=0)
+
+
+def uniform_batch(*, num_heads: int, dtype: str, block_size: int, bs: int = 52,
+                  ctx: int = 16384, seed: int = 2, num_segments: int = 0,
+                  poison: bool = False, name: Optional[str] = None) -> Workload:
+    """bs requests of identical length ``ctx``, qlen = 1, random page permutation."""
+    return make_workload(name=name or f"bs{bs}_ctx{ctx}_h{num_heads}_{dtype}_blk{block_size}",
+                         seq_lens=[ctx] * bs, num_heads=num_heads, block_size=block_size,
+                         dtype=dtype, seed=seed, num_segments=num_segments, poison=poison)
+
+
+def bs52_h16_bf16(bs: int = 52, ctx: int = 16384) -> Workload:
+    return uniform_batch(num_heads=16, dtype="bf16", block_size=64, bs=bs, ctx=ctx, seed=2)
+
+
+def bs52_fp8(num_heads: int = 48, bs: int = 52, ctx: int = 16384) -> Workload:
+    return uniform_batch(num_heads=num_heads, dtype="fp8_e4m3", block_size=64, bs=bs, ctx=ctx,
+                         seed=3)
+
+
+def bs52_h128_bf16(bs: int = 52, ctx: int = 16384) -> Workload:
+    return uniform_batch(num_heads=128, dtype="bf16", block_size=256, bs=bs, ctx=ctx, seed=4)
+
+
+def ragged_lengths(num_reqs: int, max_len: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Log-uniform lengths in [1, max_len] and qlen ~ U{1..4}; len >= qlen."""
+    g = _gen(seed + 1000)
+    u = torch.rand(num_reqs, generator=g, dtype=torch.float64).numpy()
+    qlens = torch.randint(1, 5, (num_reqs,), generator=g).numpy().astype(np.int64)
+    lens = np.rint(np.exp(u * math.log(max_len))).astype(np.int64)
+    lens = np.clip(lens, np.maximum(1, qlens), max_len)
+    return lens, qlens
+
+
+def ragged_h96_fp8(num_reqs: int = 128, max_len: int = 32768, num_heads: int = 96,
+                   seed: int = 5) -> Workload:
+    """Ragged causal batch: log-uniform lengths, qlen 1..4, H=96, fp8, sinks."""
+    lens, qlens = ragged_lengths(num_reqs, max_len, seed)
+    return make_workload(name=f"ragged{num_reqs}_max{max_len}_h{num_heads}_fp8",
+                         seq_lens=lens, qlens=qlens, num_heads=num_heads, block_size=64,
+                         dtype="fp8_e4m3", causal=True, sinks=True, seed=seed, poison=True)
+
+
+def with_(w: Workload, **kw) -> Workload:
+    return replace(w, **kw)
