@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""MLA paged decode benchmark on one MI355X.
+
+One step = one full decode of the batch: the segment kernel (paged KV stream,
+QK^T, base-2 online softmax, P.V, per-segment partials) and the merge kernel
+(output + natural-log LSE), i.e. mla_decode through the C ABI.
+
+Default workload: bs=52 requests, qlen=1, 16 heads, 16384 KV tokens per
+request, bf16 q and latent cache ~N(0,1), block 64 = TILE 64, random block
+table permutation, segment count from the planner, scale 1/sqrt(192).
+Inputs are synthetic (seeded) and resident in HBM before timing starts; two
+cache copies alternate between steps so no step reuses the previous step's
+cache lines from the 256 MB last-level cache.
+
+Prints ONE JSON line.  Extra configurations (--extra) are appended under
+"extra" in the same line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per MLA decode step and effective KV HBM GB/s (bs=52, 16K ctx, H=16..128)"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (num_heads, dtype, block, seed)
+    "bs52_ctx16k_h16_bf16_blk64": (16, "bf16", 64, 2),
+    "bs52_ctx16k_h48_fp8_blk64": (48, "fp8_e4m3", 64, 3),
+    "bs52_ctx16k_h64_fp8_blk64": (64, "fp8_e4m3", 64, 3),
+    "bs52_ctx16k_h128_bf16_blk256": (128, "bf16", 256, 4),
+}
+DEFAULT = "bs52_ctx16k_h16_bf16_blk64"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--extra", action="store_true", help="also time the other bs=52 workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-reqs", type=int, default=4)
+    ap.add_argument("--num-segments", type=int, default=0)
+    return ap.parse_args()
+
+
+def build_inputs(name, torch, mi):
+    H, dtype, block, seed = WORKLOADS[name]
+    w = mi.uniform_batch(num_heads=H, dtype=dtype, block_size=block, bs=52, ctx=16384, seed=seed,
+                         name=name)
+    d = mi.to_torch(w, "cuda")
+    # a second cache copy (same contents, other addresses) for alternating steps
+    d2 = dict(d)
+    d2["kv_cache"] = d["kv_cache"].clone()
+    return w, [d, d2]
+
+
+def time_workload(name, args, torch, m, mi, want_roofline):
+    w, ds = build_inputs(name, torch, mi)
+    esz = 2 if w.kv_dtype == "bf16" else 1
+    kv_bytes = w.kv_bytes_touched()
+    calls = [mi.call_args(w, d) for d in ds]
+    p = m.make_problem(**calls[0], num_segments=args.num_segments)
+    S = m.resolve_num_segments(p)
+    ws = torch.empty(m.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.num_tokens, w.num_heads, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.num_tokens, w.num_heads), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        m.decode(**calls[i & 1], num_segments=S, out=out, lse=lse, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    res = {"workload": name, "num_heads": w.num_heads, "dtype": w.kv_dtype, "num_segments": S,
+           "us_per_step": ms * 1e3, "kv_bytes": kv_bytes,
+           "eff_kv_GBps": kv_bytes / (ms * 1e-3) / 1e9,
+           "frac_of_hbm_peak": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if not want_roofline:
+        return w, res, None
+
+    # Segment kernel alone (the dominant kernel), timed with events on the
+    # stream it is launched on.
+    T, H = w.num_tokens, w.num_heads
+    so = torch.empty((T, H, S, 512), dtype=torch.float32, device="cuda")
+    sm = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
+    se = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
+    for i in range(args.warmup):
+        m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
+                          segm_expsum=se, stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
+                          segm_expsum=se, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    seg_ms = e0.elapsed_time(e1) / args.steps
+    # Algorithmic bytes of one segment-kernel launch: every cache row once,
+    # q once, the fp32 partials of every valid segment written once.
+    import mla_paged_decode_02_amd as mm
+    valid = sum(len(mm.segment_bounds(int(L), S, w.tile_size or mm.tile_size_for_block(w.block_size)))
+                for L in w.seq_lens)
+    q_bytes = T * H * 576 * esz
+    part_bytes = valid * H * (512 + 2) * 4
+    alg = kv_bytes + q_bytes + part_bytes
+    achieved = alg / (seg_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "segment_kernel", "kernel_us": round(seg_ms * 1e3, 2),
+            "algorithmic_bytes": alg}
+    res["segment_kernel_us"] = seg_ms * 1e3
+    res["merge_and_launch_us"] = (ms - seg_ms) * 1e3
+    return w, res, roof
+
+
+def cpu_baseline(w, nreq):
+    """The fp64 oracle on `nreq` requests of the same batch, scaled to GB/s of
+    KV rows (the oracle as it stands, host cores)."""
+    import numpy as np
+    from oracle import mla_oracle as orc
+
+    reqs = list(range(min(nreq, w.num_reqs)))
+    t = time.perf_counter()
+    orc.mla_decode(w, reqs=reqs)
+    dt = time.perf_counter() - t
+    esz = 2 if w.kv_dtype == "bf16" else 1
+    bytes_ = sum(int(w.seq_lens[r]) for r in reqs) * 576 * esz
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s (effective KV)", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(reqs)} of {w.num_reqs} requests ({len(reqs) * int(w.seq_lens[0])} KV rows, "
+                      f"{w.num_heads} heads), fp64 NumPy oracle incl. page gather: {dt:.2f} s; "
+                      f"full step would take {dt * w.num_reqs / len(reqs):.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (one GPU per box, "
+              "no multi-GPU path in this library)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mla_inputs as mi
+    import mla_paged_decode_02_amd as m
+
+    m.lib()
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    w, res, roof = time_workload(args.workload, args, torch, m, mi, want_roofline=True)
+    extra = []
+    if args.extra:
+        for name in WORKLOADS:
+            if name == args.workload:
+                continue
+            torch.cuda.empty_cache()
+            _, r2, _ = time_workload(name, args, torch, m, mi, want_roofline=False)
+            extra.append(r2)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_reqs)
+    line = {
+        "metric": METRIC,
+        "value": round(res["eff_kv_GBps"], 1),
+        "unit": "GB/s (effective KV bytes / step time)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["us_per_step"] / 1e3, 5),
+        "us_per_step": round(res["us_per_step"], 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) q and latent cache, random page permutation)",
+        "config": {"workload": res["workload"], "batch": 52, "qlen": 1, "kv_tokens_per_request": 16384,
+                   "num_heads": res["num_heads"], "block_size": WORKLOADS[res["workload"]][2],
+                   "num_segments": res["num_segments"], "parallelism": "single GPU"},
+        "frac_of_hbm_peak": round(res["frac_of_hbm_peak"], 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+        "wall_s": round(time.time() - t0, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

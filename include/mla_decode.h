@@ -1,0 +1,200 @@
+/*
+ * mla_decode.h -- C ABI of an MI355X (gfx950) library for multi-head latent
+ * attention (MLA) decode over a paged latent KV cache, split along the key
+ * axis into segments whose base-2 partials are merged into the output plus a
+ * natural-log LSE.
+ *
+ * Pages this interface follows (cited by page title and section):
+ *  - vLLM API page "vllm.v1.attention.ops.rocm_aiter_mla_merge": module
+ *    description (segment partition tiles_per_segment =
+ *    cdiv(seq_len, NUM_SEGMENTS * TILE_SIZE); base-2 partials; natural-log LSE
+ *    for a later cross-rank merge) and merge_mla_segments_triton (partials
+ *    [T, H, S, 512], output [T, H, 512] in out_dtype, lse [T, H] fp32).
+ *  - Source page "rocm_aiter_mla.py" (vLLM AITER MLA backend):
+ *    _segmented_mla_page_size (TILE = min(128, largest power-of-two divisor of
+ *    the block)), _forward_segmented_dcp_verify (q = [q_nope(512) || q_pe(64)],
+ *    cache viewed as [blocks, page, 576], kv_descale scales the cache, causal
+ *    rows of a multi-token query block), dcp_local_verify_row_lens (row t of a
+ *    qlen-token block sees positions [0, seq_len - qlen + t]) and
+ *    _expand_page_indices_kernel (block table strides come from the caller).
+ *  - vLLM API page "vllm.v1.attention.backends.mla.rocm_aiter_mla_sparse":
+ *    ROCMAiterMLASparseImpl.__init__ (sinks are fp32, one per head) and
+ *    _forward_mla (sink folded in after the merge with logaddexp).
+ *
+ * Conventions
+ *  - Every pointer named "device" is GPU memory owned by the caller; the
+ *    library never allocates, frees or retains it.  "stream" is a hipStream_t
+ *    (NULL = the legacy default stream).  Calls are stream-ordered and
+ *    asynchronous: no call reads device memory on the host or synchronises, so
+ *    every launch is graph-capturable.
+ *  - All argument checking happens on the host before any launch.  On error
+ *    nothing is launched and a negative status is returned; mla_last_error()
+ *    gives a message (thread-local).
+ *  - Device-side metadata (seq_lens, qo_indptr, block ids) cannot be checked
+ *    without a sync.  The kernels clamp it so that no access leaves the
+ *    buffers the descriptor describes; a request whose metadata is out of range
+ *    produces NaN in its outputs instead.
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1) /* shape, stride, alignment, NULL, tile or S */
+#define MLA_ERR_UNSUPPORTED (-2) /* head count > 128 or a dtype pair not offered */
+#define MLA_ERR_WORKSPACE (-3)   /* workspace missing or too small */
+#define MLA_ERR_HIP (-4)         /* launch failed; message carries the HIP error */
+
+/* Element types. */
+#define MLA_DTYPE_BF16 1
+#define MLA_DTYPE_FP8_E4M3 2 /* OCP float8 e4m3 "fn" (max 448, no inf) */
+#define MLA_DTYPE_FP16 3     /* output only */
+#define MLA_DTYPE_FP32 4     /* output only */
+
+#define MLA_HEAD_DIM 576     /* kv_lora_rank 512 + rope 64 */
+#define MLA_KV_LORA_RANK 512 /* V is the first 512 dims of each cache row */
+#define MLA_MAX_HEADS 128
+#define MLA_MAX_SEGMENTS 256
+#define MLA_MAX_TILE 128
+
+/*
+ * One decode batch.  Set struct_size = sizeof(mla_problem); zero-fill unused
+ * fields.  Rows of a request: its qlen new query tokens x num_heads.
+ */
+typedef struct mla_problem {
+  size_t struct_size;
+
+  int32_t num_tokens;   /* T: query tokens in the batch (sum of qlen) */
+  int32_t num_heads;    /* H: 1..128 */
+  int32_t num_reqs;     /* R: requests */
+  int32_t head_dim;     /* must be 576 */
+  int32_t kv_lora_rank; /* must be 512 */
+
+  /* q: device [T, H, 576] of q_dtype.  Element strides; the last dim is
+   * contiguous.  Base 16-byte aligned, strides multiples of 16 bytes. */
+  const void* q;
+  int32_t q_dtype; /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3 (must equal kv_dtype) */
+  int64_t q_stride_token;
+  int64_t q_stride_head;
+  const float* q_scale; /* device fp32 scalar: real q = code * q_scale; NULL = 1 */
+
+  /* Paged cache: device [num_blocks, block_size, 576] of kv_dtype, contiguous,
+   * 16-byte aligned.  Row j of request r lives in block
+   * block_table[r, j / block_size] at offset j % block_size. */
+  const void* kv_cache;
+  int32_t kv_dtype;      /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3 */
+  int32_t block_size;    /* >= 1 */
+  int64_t num_blocks;    /* >= 1 */
+  const float* kv_scale; /* device fp32 scalar: real row = code * kv_scale; NULL = 1 */
+
+  /* block_table: device int32, element strides (a view: both strides used). */
+  const int32_t* block_table;
+  int64_t bt_stride_row;
+  int64_t bt_stride_col;
+  int32_t max_blocks_per_req; /* columns of the table; >= cdiv(max_seq_len, block_size) */
+
+  /* seq_lens: device int32 [R], KV length of each request including its new
+   * tokens.  qo_indptr: device int32 [R+1] (query tokens of request r are
+   * [qo_indptr[r], qo_indptr[r+1])), or NULL for one token per request (T == R). */
+  const int32_t* seq_lens;
+  const int32_t* qo_indptr;
+
+  /* Host-side bounds (no device read is ever made for them). */
+  int32_t max_qlen;     /* >= every qlen; 1 when qo_indptr is NULL */
+  int32_t max_seq_len;  /* >= every seq_len */
+  int64_t sum_seq_lens; /* optional hint for the planner (0 = assume R * max_seq_len) */
+
+  int32_t causal;      /* nonzero: row i of a qlen block sees seq_len - qlen + i + 1 keys */
+  float softmax_scale; /* scores = softmax_scale * (q . row) over all 576 dims */
+  int32_t tile_size;   /* 0 = min(128, largest power-of-two divisor of block_size);
+                          else a power of two <= 128 dividing block_size */
+  int32_t num_segments; /* S >= 1 (mla_decode also accepts 0 = planner's choice) */
+} mla_problem;
+
+/*
+ * Host-only check of a descriptor (no GPU call).  Returns MLA_OK or an error.
+ * require_segments: nonzero -> num_segments must be >= 1.
+ */
+int mla_validate(const mla_problem* p, int require_segments);
+
+/*
+ * Segment partials.  Partition (per request, from its seq_len): TILE as
+ * above, tps = cdiv(seq_len, S * TILE); segment s covers positions
+ * [s*tps*TILE, min((s+1)*tps*TILE, seq_len)) and is valid iff its start is
+ * < seq_len.  For every query row (t, h) and valid segment s, with
+ * x_j = softmax_scale * log2(e) * (q . row_j) over the positions j of the
+ * segment that the row sees:
+ *   segm_max[t,h,s]    = max_j x_j                           (base 2)
+ *   segm_expsum[t,h,s] = sum_j 2^(x_j - segm_max)
+ *   segm_output[t,h,s] = sum_j 2^(x_j - segm_max) * V_j       (unnormalised,
+ *                        dequantised units, V_j = row_j[0:512])
+ * A valid segment with no visible position (causal) is (0 vector, -inf, 0).
+ * Slots of invalid segments are left untouched.
+ * Buffers (device fp32, contiguous): segm_output [T, H, S, 512],
+ * segm_max [T, H, S], segm_expsum [T, H, S].
+ */
+int mla_decode_segments(const mla_problem* p, float* segm_output, float* segm_max,
+                        float* segm_expsum, void* stream);
+
+/*
+ * Merge of segment partials.  part_lens: device int32 [T], the length the
+ * partition of token t was built from (its request's seq_len).  For each (t, h)
+ * over the valid segments: M = max_s m_s, L = sum_s l_s 2^(m_s - M),
+ * out = sum_s acc_s 2^(m_s - M) / L, lse = ln2 * (M + log2 L).  A row with no
+ * key gets out = 0, lse = -inf.  With sinks (device fp32 [H], or NULL):
+ * lse' = logaddexp(lse, sink[h]), out' = out * exp(lse - lse') (0 for rows
+ * without keys).  out: device [T, H, 512] of out_dtype (BF16 rounded to
+ * nearest even, FP16 or FP32), lse: device fp32 [T, H].  Contiguous.
+ */
+int mla_merge_segments(const float* segm_output, const float* segm_max, const float* segm_expsum,
+                       const int32_t* part_lens, int32_t num_tokens, int32_t num_heads,
+                       int32_t num_segments, int32_t kv_lora_rank, int32_t tile_size,
+                       const float* sinks, void* out, int32_t out_dtype, float* lse,
+                       void* stream);
+
+/*
+ * Fused decode: segments + merge in two stream-ordered launches, the partials
+ * living in the caller's workspace (>= mla_decode_workspace_bytes(p) bytes,
+ * 256-byte aligned).  num_segments == 0 lets the planner choose S.
+ * sinks / out / out_dtype / lse as for mla_merge_segments.
+ */
+int mla_decode(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace mla_decode needs for p (uses the planner when num_segments == 0).
+ * Returns 0 and sets *bytes, or an error. */
+int mla_decode_workspace_bytes(const mla_problem* p, size_t* bytes);
+
+/* The S mla_decode would use for p (host only after the first call on a
+ * device: reads the CU count once). Returns S >= 1 or an error. */
+int mla_resolve_num_segments(const mla_problem* p);
+
+/* Planner (pure host): S so that request x segment work items fill num_cus
+ * compute units; clamped to [1, min(MLA_MAX_SEGMENTS, cdiv(max_seq_len, TILE))]. */
+int mla_plan_num_segments(int32_t num_reqs, int32_t max_seq_len, int64_t sum_seq_lens,
+                          int32_t num_heads, int32_t max_qlen, int32_t tile_size,
+                          int32_t kv_dtype, int32_t num_cus);
+
+/* TILE for a block size (min(128, largest power-of-two divisor)); error if < 1. */
+int mla_tile_size_for_block(int32_t block_size);
+
+/* Host partition of one request: writes the valid segments' [start, end) into
+ * starts/ends (capacity num_segments each, may be NULL) and returns their count. */
+int mla_segment_bounds(int32_t seq_len, int32_t num_segments, int32_t tile_size,
+                       int32_t* starts, int32_t* ends);
+
+const char* mla_status_string(int status);
+const char* mla_last_error(void);
+int mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_DECODE_H_ */

@@ -269,3 +269,38 @@ def ragged_h96_fp8(num_reqs: int = 128, max_len: int = 32768, num_heads: int = 9
 
 def with_(w: Workload, **kw) -> Workload:
     return replace(w, **kw)
+
+
+def to_torch(w: Workload, device="cuda") -> dict:
+    """Upload a workload's codes and metadata as device tensors (codes keep
+    their bits: bf16 as torch.bfloat16, fp8 as torch.float8_e4m3fn)."""
+    def codes(a: np.ndarray, dtype: str) -> torch.Tensor:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        else:
+            t = t.view(torch.uint8).view(torch.float8_e4m3fn)
+        return t.to(device)
+
+    d = {
+        "q": codes(w.q, w.q_dtype),
+        "kv_cache": codes(w.kv_cache, w.kv_dtype),
+        "block_table": torch.from_numpy(np.ascontiguousarray(w.block_table)).to(device),
+        "seq_lens": torch.from_numpy(np.ascontiguousarray(w.seq_lens)).to(device),
+        "qo_indptr": torch.from_numpy(np.ascontiguousarray(w.qo_indptr)).to(device),
+        "q_scale": None if w.q_scale is None else torch.tensor([w.q_scale], dtype=torch.float32, device=device),
+        "kv_scale": None if w.kv_scale is None else torch.tensor([w.kv_scale], dtype=torch.float32, device=device),
+        "sinks": None if w.sinks is None else torch.from_numpy(np.ascontiguousarray(w.sinks)).to(device),
+    }
+    return d
+
+
+def call_args(w: Workload, d: dict, *, use_indptr: Optional[bool] = None) -> dict:
+    """Keyword arguments for the library's decode entry points."""
+    if use_indptr is None:
+        use_indptr = w.max_qlen != 1 or w.num_tokens != w.num_reqs
+    return dict(q=d["q"], kv_cache=d["kv_cache"], block_table=d["block_table"],
+                seq_lens=d["seq_lens"], softmax_scale=w.softmax_scale,
+                max_seq_len=w.max_seq_len, qo_indptr=d["qo_indptr"] if use_indptr else None,
+                max_qlen=w.max_qlen if use_indptr else None, causal=w.causal,
+                q_scale=d["q_scale"], kv_scale=d["kv_scale"], tile_size=w.tile_size)

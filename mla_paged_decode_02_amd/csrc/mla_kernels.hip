@@ -1,0 +1,686 @@
+// HIP kernels for MLA paged decode on gfx950 (MI355X).
+//
+// Segment kernel: one workgroup per (request, segment, row chunk).  A row is
+// one (query token, head) pair of the request; a wave owns 16 rows.  All waves
+// of a workgroup stream the segment's 576-wide cache rows HBM -> LDS once,
+// 32 tokens per tile, through direct global->LDS loads into a ring of tiles,
+// and every wave computes its rows against each tile:
+//
+//   S^T[token, row] = K . Q^T    MFMA 16x16x32 (bf16, or fp8 x fp8)
+//   base-2 online softmax        exp2, max over the tile via lane shuffles
+//   O^T[dim, row]  += V^T . P^T  MFMA 16x16x32 bf16; V^T comes straight from
+//                                the row-major tile with the LDS transpose
+//                                reads (ds_read_b64_tr_b16 / _tr_b8)
+//
+// The same tile bytes serve as K (all 576 dims) and V (the first 512), as the
+// AITER MLA backend's segmented call does (source page "rocm_aiter_mla.py",
+// _forward_segmented_dcp_verify: one [blocks, page, 576] cache view, latent
+// rank 512 + rope 64).  No head count is folded into 16-head pseudo-batches:
+// every row of a request reads the tile from LDS, so the cache bytes of a
+// request leave HBM once per segment regardless of the head count.
+//
+// Partials are base 2 and unnormalised; the merge kernel turns them into the
+// output and a natural-log LSE (vLLM API page
+// "vllm.v1.attention.ops.rocm_aiter_mla_merge", merge_mla_segments_triton)
+// and folds in optional per-head sinks (vLLM API page
+// "vllm.v1.attention.backends.mla.rocm_aiter_mla_sparse", _forward_mla).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// The softmax reference max moves only past this many base-2 units (p <= 2^8).
+constexpr float kLazy = 8.0f;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most `ahead` tiles of this wave's DMA loads are in flight.
+template <int PER_TILE, int MAX_AHEAD>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  if constexpr (MAX_AHEAD >= 6) { if (ahead >= 6) { wait_vmcnt<(6 * PER_TILE < 63 ? 6 * PER_TILE : 63)>(); return; } }
+  if constexpr (MAX_AHEAD >= 5) { if (ahead == 5) { wait_vmcnt<(5 * PER_TILE < 63 ? 5 * PER_TILE : 63)>(); return; } }
+  if constexpr (MAX_AHEAD >= 4) { if (ahead == 4) { wait_vmcnt<(4 * PER_TILE < 63 ? 4 * PER_TILE : 63)>(); return; } }
+  if constexpr (MAX_AHEAD >= 3) { if (ahead == 3) { wait_vmcnt<(3 * PER_TILE < 63 ? 3 * PER_TILE : 63)>(); return; } }
+  if constexpr (MAX_AHEAD >= 2) { if (ahead == 2) { wait_vmcnt<(2 * PER_TILE < 63 ? 2 * PER_TILE : 63)>(); return; } }
+  if constexpr (MAX_AHEAD >= 1) { if (ahead == 1) { wait_vmcnt<(PER_TILE < 63 ? PER_TILE : 63)>(); return; } }
+  wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// LDS tile layout (32 tokens).  The 512 latent dims (also V) and the 64 rope
+// dims of a row live in two regions so that one DMA instruction (64 lanes x
+// 16 B) covers whole rows:
+//   bf16: V region 32 x 1024 B, rope region 32 x 128 B at +32 KiB
+//   fp8 : V region 32 x  512 B, rope region 32 x  64 B at +16 KiB
+// 16-byte chunks are XOR-swizzled per row.  In the V region chunk c of row r
+// sits at c ^ swz_v(r), swz_v a permutation of 0..15 within each 16-row block
+// (((r & 7) << 1) | bit 3 of r), flipped in bit 0 for the second block, so
+// that (a) the 16 rows a K read touches, (b) the 8 rows x 2 chunks of a
+// 16-bit transpose read and (c) the 16 rows of an 8-bit transpose read each
+// hit distinct bank groups.  Rope chunks use swz_r(r) = (r >> 1) & 7 (bf16) or
+// (r >> 2) & 3 (fp8), distinct within each group of rows one read touches.
+template <bool FP8>
+struct KvFmt;
+template <>
+struct KvFmt<false> {  // bf16
+  static constexpr int kRowBytes = 1152;   // in the cache
+  static constexpr int kVPitch = 1024;     // LDS V region row pitch
+  static constexpr int kRopePitch = 128;   // LDS rope region row pitch
+  static constexpr int kVChunks = 64;
+  static constexpr int kRopeChunks = 8;
+  __device__ static int swz_r(int r) { return (r >> 1) & 7; }
+};
+template <>
+struct KvFmt<true> {  // fp8
+  static constexpr int kRowBytes = 576;
+  static constexpr int kVPitch = 512;
+  static constexpr int kRopePitch = 64;
+  static constexpr int kVChunks = 32;
+  static constexpr int kRopeChunks = 4;
+  __device__ static int swz_r(int r) { return (r >> 2) & 3; }
+};
+
+__device__ __forceinline__ int swz_v(int r) { return ((((r & 7) << 1) | ((r >> 3) & 1)) ^ ((r >> 4) & 1)); }
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&p)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)p[i];
+  return r;
+}
+
+// 8 fp8-e4m3 codes (two dwords) -> 8 bf16 values (exact: e4m3 fits in bf16).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 v) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Segment kernel
+// ---------------------------------------------------------------------------
+// Hides a value from the optimiser for one use site: offsets derived from it
+// are recomputed where needed instead of being hoisted out of the tile loop
+// into dozens of long-lived registers.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_load(const char* base, int off) {
+  return *(const LDS_AS T*)(base + off);
+}
+
+// NW waves x RG row groups of 16 rows per workgroup.
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG>
+__global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
+  using F = KvFmt<FP8>;
+  constexpr int kRowBytes = F::kRowBytes;
+  constexpr int kVRegion = kTileTokens * F::kVPitch;
+  constexpr int kTileBytes = kTileTokens * kRowBytes;  // 36864 (bf16) / 18432 (fp8)
+  constexpr int kRowsPerV = 1024 / F::kVPitch;         // rows per V-region DMA instruction
+  constexpr int kNIV = kTileTokens / kRowsPerV;        // V-region DMA instructions
+  constexpr int kNI = kTileBytes / 1024;               // all DMA instructions per tile
+  constexpr int kNIw = kNI / NW;                       // per wave, lower bound
+  constexpr int kNIwMax = (kNI + NW - 1) / NW;
+  constexpr int kRowsWG = 16 * RG * NW;
+  static_assert(kTileBytes % 1024 == 0, "tile must be whole DMA instructions");
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][kTileBytes];
+  __shared__ int phys_rows[CONTIG ? 1 : kTileTokens];
+
+  const int s = blockIdx.x;
+  const int r = blockIdx.y;
+  const int chunk = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int g = lane >> 4;
+  const int n = lane & 15;
+
+  // ---- request geometry (uniform over the workgroup) ----
+  int t0 = r, qlen = 1;
+  if (p.qo_indptr) {
+    t0 = p.qo_indptr[r];
+    qlen = p.qo_indptr[r + 1] - t0;
+    if (t0 < 0 || qlen < 0 || qlen > p.max_qlen || t0 + qlen > p.num_tokens) return;
+  }
+  const int H = p.num_heads;
+  const int M = qlen * H;
+  const int row0 = chunk * kRowsWG;
+  if (row0 >= M) return;
+
+  const int L = p.seq_lens[r];
+  if (L <= 0) return;  // no valid segment
+  // A length past the block table is reported as NaN; rows beyond the table
+  // are never read.
+  const int cap = p.bt_cols * p.block_size;
+  bool bad = L > cap;
+  const int span = cdiv(L, p.num_segments * p.tile) * p.tile;
+  const int seg_start = s * span;
+  if (seg_start >= L) return;  // invalid segment: its slot is never read
+  const int seg_end = min(seg_start + span, L);
+
+  // The workgroup's last row decides how far its rows can see.
+  const int last_row = min(row0 + kRowsWG, M) - 1;
+  const int lim_wg = p.causal ? (L - qlen + last_row / H + 1) : L;
+  const int eff_end = min(min(seg_end, lim_wg), cap);
+  const int ntiles = eff_end > seg_start ? cdiv(eff_end - seg_start, kTileTokens) : 0;
+
+  // ---- this lane's query rows (one per row group) ----
+  int ti[RG], hh[RG], end_row[RG];
+  bool rok[RG];
+#pragma unroll
+  for (int q = 0; q < RG; ++q) {
+    const int row = row0 + (wave * RG + q) * 16 + n;
+    rok[q] = row < M;
+    ti[q] = rok[q] ? row / H : 0;
+    hh[q] = rok[q] ? row - ti[q] * H : 0;
+    const int lim = rok[q] ? (p.causal ? max(0, L - qlen + ti[q] + 1) : L) : 0;
+    end_row[q] = min(seg_end, lim);
+  }
+  const bool wave_has_rows = row0 + wave * RG * 16 < M;
+
+  const float qs = p.q_scale ? *p.q_scale : 1.0f;
+  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
+  const float sl2 = p.softmax_scale * kLog2e * qs * ks;
+
+  // ---- Q^T operand: lane (g, n) holds row n, dims 32c + 8g .. +7 ----
+  typedef typename std::conditional<FP8, long, bf16x8>::type QOp;
+  QOp qop[RG][18];
+#pragma unroll
+  for (int q = 0; q < RG; ++q) {
+    const int64_t qoff = (int64_t)(t0 + ti[q]) * p.q_stride_token + (int64_t)hh[q] * p.q_stride_head;
+#pragma unroll
+    for (int c = 0; c < 18; ++c) {
+      if constexpr (FP8) {
+        const uint8_t* qp = (const uint8_t*)p.q + qoff + 32 * c + 8 * g;
+        qop[q][c] = rok[q] ? *(const long*)qp : 0;
+      } else {
+        const __bf16* qp = (const __bf16*)p.q + qoff + 32 * c + 8 * g;
+        const u32x4 v = rok[q] ? *(const u32x4*)qp : u32x4{0, 0, 0, 0};
+        qop[q][c] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  }
+  wait_vmcnt<0>();  // q is in registers before the DMA stream starts
+
+  // ---- DMA of one 32-token tile into ring slot b ----
+  // Instruction kk < kNIV fills V-region row(s) kk*kRowsPerV.., later ones the
+  // rope region; lane lambda writes LDS byte 16*lambda of its instruction's
+  // 1 KiB and loads the logical chunk that the swizzle stores there.
+  auto issue_tile = [&](int k, int b) {
+    const int tile_start = seg_start + k * kTileTokens;
+    const int nvalid = min(kTileTokens, eff_end - tile_start);
+    const char* base = nullptr;
+    if constexpr (CONTIG) {
+      const int blk_i = tile_start / p.block_size;
+      int blk = p.block_table[(int64_t)r * p.bt_stride_row + (int64_t)blk_i * p.bt_stride_col];
+      if (blk < 0 || blk >= p.num_blocks) { blk = 0; bad = true; }
+      const int64_t phys0 = (int64_t)blk * p.block_size + (tile_start - blk_i * p.block_size);
+      base = p.kv + phys0 * kRowBytes;
+    } else {
+      // Rows of a tile span several pages: thread j < 32 resolves tile row j.
+      __syncthreads();  // previous readers of phys_rows are done
+      if (threadIdx.x < kTileTokens) {
+        const int j = tile_start + ((int)threadIdx.x < nvalid ? (int)threadIdx.x : 0);
+        const int blk_i = j / p.block_size;
+        const int blk = p.block_table[(int64_t)r * p.bt_stride_row + (int64_t)blk_i * p.bt_stride_col];
+        phys_rows[threadIdx.x] =
+            (blk < 0 || blk >= p.num_blocks) ? -1 : blk * p.block_size + (j - blk_i * p.block_size);
+      }
+      __syncthreads();
+    }
+    const int ln = opaque(lane);
+#pragma unroll
+    for (int i = 0; i < kNIwMax; ++i) {
+      const int kk = i * NW + wave;
+      if (kk < kNI) {
+        int trow, gbyte;
+        if (kk < kNIV) {
+          trow = kk * kRowsPerV + ln / F::kVChunks;
+          const int cpos = ln % F::kVChunks;
+          gbyte = 16 * (cpos ^ swz_v(trow));
+        } else {
+          constexpr int kRowsPerRope = 64 / F::kRopeChunks;
+          trow = (kk - kNIV) * kRowsPerRope + ln / F::kRopeChunks;
+          const int cpos = ln % F::kRopeChunks;
+          gbyte = kKvRank * (FP8 ? 1 : 2) + 16 * (cpos ^ F::swz_r(trow));
+        }
+        const int rr = trow < nvalid ? trow : 0;
+        const char* src;
+        if constexpr (CONTIG) {
+          src = base + rr * kRowBytes + gbyte;
+        } else {
+          int pr = phys_rows[rr];
+          if (pr < 0) { pr = 0; bad = true; }
+          src = p.kv + (int64_t)pr * kRowBytes + gbyte;
+        }
+        __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)&lds[b][kk * 1024], 16, 0, 0);
+      }
+    }
+  };
+
+  // ---- running state ----
+  f32x4 acc[RG][32];
+#pragma unroll
+  for (int q = 0; q < RG; ++q)
+#pragma unroll
+    for (int d = 0; d < 32; ++d) acc[q][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[RG], m_true[RG], l_run[RG];
+#pragma unroll
+  for (int q = 0; q < RG; ++q) { m_run[q] = m_true[q] = -INFINITY; l_run[q] = 0.f; }
+
+  // Per-lane LDS read geometry (see the layout note above KvFmt).
+  // K reads: lane (g, t = n) reads tile row 16b + n.
+  int kv_base[2], kv_x[2], kr_base[2], kr_x[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int lrow = 16 * b + n;
+    kv_base[b] = lrow * F::kVPitch;
+    kr_base[b] = kVRegion + lrow * F::kRopePitch;
+    if constexpr (FP8) {
+      // logical chunk 2c + g/2, 8-byte half g & 1
+      kv_x[b] = (g >> 1) ^ swz_v(lrow);
+      kr_x[b] = (g >> 1) ^ F::swz_r(lrow);
+      kv_base[b] += 8 * (g & 1);
+      kr_base[b] += 8 * (g & 1);
+    } else {
+      // logical chunk 4c + g
+      kv_x[b] = g ^ swz_v(lrow);
+      kr_x[b] = g ^ F::swz_r(lrow);
+    }
+  }
+  // V^T transpose reads.
+  int vt_base[2], vt_x[2];
+  if constexpr (FP8) {
+    // address lane 16g + 2e + j: k-slot e = (block e/4, A-row 4g + e%4), dims 16db + 8j
+    const int e = (lane >> 1) & 7, j = lane & 1;
+    const int vrow = 16 * (e >> 2) + 4 * g + (e & 3);
+    vt_base[0] = vrow * F::kVPitch + 8 * j;
+    vt_x[0] = swz_v(vrow);
+    vt_base[1] = vt_x[1] = 0;
+  } else {
+    // address lane 16g + 4i + j: A-row 4g + i of block 0 / 1, dims 16db + 4j
+    const int i4 = (lane >> 2) & 3, j = lane & 3;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int vrow = 16 * rd + 4 * g + i4;
+      vt_base[rd] = vrow * F::kVPitch + 8 * (j & 1);
+      vt_x[rd] = (j >> 1) ^ swz_v(vrow);
+    }
+  }
+
+  // ---- pipeline ----
+#pragma unroll
+  for (int k = 0; k < NBUF - 1; ++k)
+    if (k < ntiles) issue_tile(k, k);
+
+  for (int k = 0; k < ntiles; ++k) {
+    wait_tiles<kNIw, NBUF - 2>(min(NBUF - 2, ntiles - 1 - k));
+    __syncthreads();
+    if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+    if (!wave_has_rows) continue;
+
+    const char* buf = lds[k % NBUF];
+    const int tile_start = seg_start + k * kTileTokens;
+    int kvb[2], kvx[2], krb[2], krx[2], vtb[2], vtx[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      kvb[b] = opaque(kv_base[b]); kvx[b] = opaque(kv_x[b]);
+      krb[b] = opaque(kr_base[b]); krx[b] = opaque(kr_x[b]);
+      vtb[b] = opaque(vt_base[b]); vtx[b] = opaque(vt_x[b]);
+    }
+
+    // S^T = K . Q^T for the two 16-token blocks: 36 (chunk, block) steps,
+    // operands prefetched kPF steps ahead.
+    typedef typename std::conditional<FP8, long, bf16x8>::type KOp;
+    constexpr int kPF = 4;
+    auto k_off = [&](int st) {
+      const int c = st >> 1, b = st & 1;
+      if (c < 16) {
+        const int lc = FP8 ? (2 * c) : (4 * c);  // logical chunk without the lane part
+        return kvb[b] + 16 * (lc ^ kvx[b]);
+      }
+      const int lc = FP8 ? (2 * (c - 16)) : (4 * (c - 16));
+      return krb[b] + 16 * (lc ^ krx[b]);
+    };
+    f32x4 sblk[RG][2];
+#pragma unroll
+    for (int q = 0; q < RG; ++q) sblk[q][0] = sblk[q][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    KOp kop[kPF];
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) kop[i] = lds_load<KOp>(buf, k_off(i));
+#pragma unroll
+    for (int st = 0; st < 36; ++st) {
+      const KOp cur = kop[st % kPF];
+      if (st + kPF < 36) kop[st % kPF] = lds_load<KOp>(buf, k_off(st + kPF));
+      const int c = st >> 1, b = st & 1;
+#pragma unroll
+      for (int q = 0; q < RG; ++q) {
+        if constexpr (FP8)
+          sblk[q][b] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur, qop[q][c], sblk[q][b], 0, 0, 0);
+        else
+          sblk[q][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qop[q][c], sblk[q][b], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Base-2 online softmax per row over this tile.  The reference max m_run
+    // only moves when the tile max exceeds it by more than kLazy (so p <= 2^kLazy);
+    // m_true tracks the exact max and the end rescales to it once.
+    bf16x8 pb[RG];
+    bool rescale = false;
+    float alpha[RG];
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      float x[8];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // score slot i: block i/4, A-row 4g + i%4
+        const int tok = tile_start + 16 * (i >> 2) + 4 * g + (i & 3);
+        const float v = (tok < end_row[q]) ? sblk[q][i >> 2][i & 3] * sl2 : -INFINITY;
+        x[i] = v;
+        mloc = fmaxf(mloc, v);
+      }
+      mloc = wave_max(mloc);
+      m_true[q] = fmaxf(m_true[q], mloc);
+      const float m_new = (mloc > m_run[q] + kLazy) ? mloc : m_run[q];
+      alpha[q] = 1.f;
+      float pv[8];
+      if (m_new == -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = 0.f;
+      } else {
+        alpha[q] = __builtin_amdgcn_exp2f(m_run[q] - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+          psum += pv[i];
+        }
+        l_run[q] = l_run[q] * alpha[q] + psum;
+      }
+      m_run[q] = m_new;
+      rescale |= alpha[q] != 1.f;
+      pb[q] = to_bf16x8(pv);
+    }
+    if (__ballot(rescale)) {
+#pragma unroll
+      for (int q = 0; q < RG; ++q)
+#pragma unroll
+        for (int d = 0; d < 32; ++d) acc[q][d] *= alpha[q];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // O^T += V^T . P^T over 32 dim blocks of 16, operands prefetched kPF ahead.
+    typedef typename std::conditional<FP8, i32x2, bf16x8>::type VRaw;
+    auto v_load = [&](int db) -> VRaw {
+      if constexpr (FP8) {
+        // logical chunk db, half j
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (LDS_AS i32x2*)(buf + vtb[0] + 16 * (db ^ vtx[0])));
+      } else {
+        // logical chunk 2db + j/2, half j & 1
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(buf + vtb[0] + 16 * ((2 * db) ^ vtx[0])));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(buf + vtb[1] + 16 * ((2 * db) ^ vtx[1])));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    VRaw vop[kPF];
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) vop[i] = v_load(i);
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const VRaw cur = vop[db % kPF];
+      if (db + kPF < 32) vop[db % kPF] = v_load(db + kPF);
+      bf16x8 va;
+      if constexpr (FP8) va = fp8x8_to_bf16x8(__builtin_bit_cast(u32x2, cur));
+      else va = cur;
+#pragma unroll
+      for (int q = 0; q < RG; ++q)
+        acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[q], acc[q][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Final exact-max correction of the lazily rescaled state.
+#pragma unroll
+  for (int q = 0; q < RG; ++q) {
+    const float f = (m_true[q] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[q] - m_true[q]);
+    l_run[q] *= f;
+#pragma unroll
+    for (int d = 0; d < 32; ++d) acc[q][d] *= f;
+  }
+
+  // ---- write this segment's partials ----
+  bad = __syncthreads_or(bad ? 1 : 0) != 0;
+#pragma unroll
+  for (int q = 0; q < RG; ++q) {
+    float l_tot = l_run[q] + __shfl_xor(l_run[q], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (!rok[q]) continue;
+    const int64_t slot = ((int64_t)(t0 + ti[q]) * H + hh[q]) * p.num_segments + s;
+    float* outp = p.seg_out + slot * kKvRank + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) *(f32x4*)(outp + 16 * db) = acc[q][db] * ks;
+    if (g == 0) {
+      p.seg_max[slot] = bad ? __builtin_nanf("") : m_true[q];
+      p.seg_sum[slot] = l_tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge kernel: one wave per (token, head); lane covers dims [8*lane, 8*lane+8).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+template <int OUT>  // 0 bf16, 1 fp16, 2 fp32
+__global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (h >= p.num_heads) return;
+  const int S = p.num_segments;
+
+  int L;
+  if (p.part_lens) {
+    L = p.part_lens[t];
+  } else if (p.qo_indptr) {
+    // request of token t: largest r with qo_indptr[r] <= t
+    int lo = 0, hi = p.num_reqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.qo_indptr[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    L = p.seq_lens[lo];
+  } else {
+    L = p.seq_lens[t];
+  }
+  int nv = 0;
+  if (L > 0) {
+    const int span = cdiv(L, S * p.tile) * p.tile;
+    nv = min(S, cdiv(L, span));
+  }
+  const int64_t base = ((int64_t)t * p.num_heads + h) * S;
+
+  // global max and error flag over the valid segments
+  float M = -INFINITY;
+  bool nan_seen = false;
+  for (int s = lane; s < nv; s += 64) {
+    const float m = p.seg_max[base + s];
+    nan_seen |= (m != m);
+    M = fmaxf(M, m);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  nan_seen = __ballot(nan_seen) != 0;
+
+  float Lsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const bool has = M > -INFINITY;
+  if (has) {
+    for (int s = lane; s < nv; s += 64) {
+      const float m = p.seg_max[base + s];
+      if (m > -INFINITY) Lsum += p.seg_sum[base + s] * exp2f(m - M);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Lsum += __shfl_xor(Lsum, o);
+    for (int s = 0; s < nv; ++s) {
+      const float m = p.seg_max[base + s];
+      if (!(m > -INFINITY)) continue;
+      const float w = exp2f(m - M);
+      const f32x4* src = (const f32x4*)(p.seg_out + (base + s) * kKvRank + 8 * lane);
+      const f32x4 a = src[0], b = src[1];
+      acc[0] += w * a[0]; acc[1] += w * a[1]; acc[2] += w * a[2]; acc[3] += w * a[3];
+      acc[4] += w * b[0]; acc[5] += w * b[1]; acc[6] += w * b[2]; acc[7] += w * b[3];
+    }
+  }
+  float lse;
+  float scale;
+  if (has) {
+    lse = kLn2 * (M + log2f(Lsum));
+    scale = 1.0f / Lsum;
+  } else {
+    lse = -INFINITY;
+    scale = 0.f;
+  }
+  if (p.sinks) {
+    const float sg = p.sinks[h];
+    const float mx = fmaxf(lse, sg);
+    const float nl = (mx == -INFINITY) ? -INFINITY : mx + log1pf(expf(-fabsf(lse - sg)));
+    scale = has ? scale * expf(lse - nl) : 0.f;
+    lse = nl;
+  }
+  if (nan_seen) { lse = __builtin_nanf(""); scale = __builtin_nanf(""); }
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = has ? acc[i] * scale : (nan_seen ? scale : 0.f);
+
+  const int64_t orow = ((int64_t)t * p.num_heads + h) * kKvRank + 8 * lane;
+  if constexpr (OUT == 0) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = (unsigned)f32_to_bf16_rne(o[2 * i]) | ((unsigned)f32_to_bf16_rne(o[2 * i + 1]) << 16);
+    *(u32x4*)((unsigned short*)p.out + orow) = v;
+  } else if constexpr (OUT == 1) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 a = (_Float16)o[2 * i], b = (_Float16)o[2 * i + 1];
+      v[i] = (unsigned)__builtin_bit_cast(unsigned short, a) | ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+    }
+    *(u32x4*)((unsigned short*)p.out + orow) = v;
+  } else {
+    f32x4* dst = (f32x4*)((float*)p.out + orow);
+    dst[0] = f32x4{o[0], o[1], o[2], o[3]};
+    dst[1] = f32x4{o[4], o[5], o[6], o[7]};
+  }
+  if (lane == 0) p.lse[(int64_t)t * p.num_heads + h] = lse;
+}
+
+template <bool FP8, int NW, int RG, bool CONTIG>
+hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
+  // LDS ring: 72 KiB for 1-2 waves (two workgroups per CU), 144 KiB for 3-4
+  // waves (one workgroup per CU).
+  constexpr int kTileBytes = kTileTokens * (FP8 ? 576 : 1152);
+  constexpr int kRing = (NW <= 2 ? 73728 : 147456) / kTileBytes;
+  dim3 grid(a.num_segments, a.num_reqs, chunks);
+  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG>), grid, dim3(64 * NW), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool FP8, bool CONTIG>
+hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, hipStream_t stream) {
+  if (sh.rows_per_wave == 2) {
+    if (sh.waves == 3) return launch_seg<FP8, 3, 2, CONTIG>(a, sh.chunks, stream);
+    return launch_seg<FP8, 4, 2, CONTIG>(a, sh.chunks, stream);
+  }
+  switch (sh.waves) {
+    case 1: return launch_seg<FP8, 1, 1, CONTIG>(a, sh.chunks, stream);
+    case 2: return launch_seg<FP8, 2, 1, CONTIG>(a, sh.chunks, stream);
+    case 3: return launch_seg<FP8, 3, 1, CONTIG>(a, sh.chunks, stream);
+    default: return launch_seg<FP8, 4, 1, CONTIG>(a, sh.chunks, stream);
+  }
+}
+
+}  // namespace
+
+SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
+  SegmentShape sh;
+  sh.fp8 = fp8;
+  const int groups = (max_qlen * num_heads + 15) / 16;
+  // groups of 16 rows -> (waves, row groups per wave)
+  if (groups <= 1)      { sh.waves = 1; sh.rows_per_wave = 1; }
+  else if (groups == 2) { sh.waves = 2; sh.rows_per_wave = 1; }
+  else if (groups == 3) { sh.waves = 3; sh.rows_per_wave = 1; }
+  else if (groups == 4) { sh.waves = 4; sh.rows_per_wave = 1; }
+  else if (groups <= 6) { sh.waves = 3; sh.rows_per_wave = 2; }
+  else                  { sh.waves = 4; sh.rows_per_wave = 2; }
+  const int per_wg = sh.waves * sh.rows_per_wave;
+  sh.chunks = (groups + per_wg - 1) / per_wg;
+  sh.contig = tile >= kTileTokens;
+  return sh;
+}
+
+hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, hipStream_t stream) {
+  if (sh.fp8) {
+    return sh.contig ? launch_seg_shape<true, true>(a, sh, stream) : launch_seg_shape<true, false>(a, sh, stream);
+  }
+  return sh.contig ? launch_seg_shape<false, true>(a, sh, stream) : launch_seg_shape<false, false>(a, sh, stream);
+}
+
+hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
+  dim3 grid(a.num_tokens, (a.num_heads + 3) / 4);
+  switch (a.out_dtype) {
+    case 0: hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

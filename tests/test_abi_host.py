@@ -1,0 +1,152 @@
+"""Host side of the C ABI (no GPU): the library loads, exports every function
+include/mla_decode.h declares, and its argument checks, partition and planner
+behave as specified.  Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import mla_paged_decode_02_amd as m
+from oracle import mla_oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mla_decode.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = m.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(L, name), f"{name} not exported"
+    assert set(names) == set(m.EXPORTED)
+    assert L.mla_version() >= 1
+
+
+def test_status_strings():
+    L = m.lib()
+    for code, name in [(0, "MLA_OK"), (-1, "MLA_ERR_INVALID_ARG"), (-2, "MLA_ERR_UNSUPPORTED"),
+                       (-3, "MLA_ERR_WORKSPACE"), (-4, "MLA_ERR_HIP")]:
+        assert L.mla_status_string(code).decode() == name
+
+
+@pytest.mark.parametrize("block", [1, 2, 3, 16, 48, 64, 96, 100, 128, 256, 544, 1024, 4096])
+def test_tile_rule_matches_oracle(block):
+    assert m.tile_size_for_block(block) == orc.tile_size_for_block(block)
+
+
+def test_tile_rule_rejects_nonpositive():
+    with pytest.raises(m.MlaError):
+        m.tile_size_for_block(0)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 7, 9, 19, 64, 256])
+@pytest.mark.parametrize("tile", [1, 4, 16, 64, 128])
+def test_segment_bounds_match_oracle(S, tile):
+    for L in [0, 1, 2, 15, 16, 17, 100, 257, 1000, 3328, 16384, 32768, 65537]:
+        assert m.segment_bounds(L, S, tile) == orc.segment_bounds(L, S, tile)
+
+
+def test_planner_fills_the_chip():
+    # uniform bs=52 x 16K: workgroups x per-CU capacity
+    assert m.plan_num_segments(52, 16384, 16, tile_size=64) == 9     # 1 wave/WG, 2 WGs/CU
+    assert m.plan_num_segments(52, 16384, 64, tile_size=64) == 4     # 4 waves/WG, 1 WG/CU
+    assert m.plan_num_segments(52, 16384, 128, tile_size=128) == 4
+    assert m.plan_num_segments(1, 100, 16, tile_size=16) == 7        # capped at cdiv(100, 16)
+    assert m.plan_num_segments(4000, 1000, 16, tile_size=64) == 1
+    # ragged: the longest request gets more segments when the mean is short
+    assert m.plan_num_segments(128, 32768, 96, max_qlen=4, tile_size=64, sum_seq_lens=400000) >= 4
+
+
+def _cpu_problem(**kw):
+    T, H, R = kw.pop("T", 2), kw.pop("H", 16), kw.pop("R", 2)
+    q = torch.zeros((T, H, 576), dtype=torch.bfloat16)
+    kv = torch.zeros((8, 16, 576), dtype=torch.bfloat16)
+    bt = torch.zeros((R, 4), dtype=torch.int32)
+    sl = torch.full((R,), 10, dtype=torch.int32)
+    p = m.make_problem(q, kv, bt, sl, softmax_scale=0.1, max_seq_len=10, num_segments=4)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _status(p, require=True):
+    return m.lib().mla_validate(ctypes.byref(p), 1 if require else 0)
+
+
+def test_validate_accepts_good_problem():
+    assert _status(_cpu_problem()) == m.MLA_OK
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 512, m.MLA_ERR_INVALID_ARG),
+    ("kv_lora_rank", 448, m.MLA_ERR_INVALID_ARG),
+    ("num_heads", 0, m.MLA_ERR_INVALID_ARG),
+    ("num_heads", 129, m.MLA_ERR_UNSUPPORTED),
+    ("q_dtype", 2, m.MLA_ERR_UNSUPPORTED),          # q fp8 with a bf16 cache
+    ("kv_dtype", 9, m.MLA_ERR_UNSUPPORTED),
+    ("block_size", 0, m.MLA_ERR_INVALID_ARG),
+    ("tile_size", 3, m.MLA_ERR_INVALID_ARG),
+    ("tile_size", 32, m.MLA_ERR_INVALID_ARG),      # does not divide block 16
+    ("num_segments", 0, m.MLA_ERR_INVALID_ARG),
+    ("num_segments", 257, m.MLA_ERR_INVALID_ARG),
+    ("max_seq_len", 100, m.MLA_ERR_INVALID_ARG),   # needs 7 blocks, table has 4
+    ("q", None, m.MLA_ERR_INVALID_ARG),
+    ("seq_lens", None, m.MLA_ERR_INVALID_ARG),
+    ("q_stride_head", 500, m.MLA_ERR_INVALID_ARG),
+    ("bt_stride_col", 0, m.MLA_ERR_INVALID_ARG),
+    ("softmax_scale", 0.0, m.MLA_ERR_INVALID_ARG),
+    ("struct_size", 8, m.MLA_ERR_INVALID_ARG),
+    ("num_tokens", 3, m.MLA_ERR_INVALID_ARG),      # no qo_indptr: T must equal R
+])
+def test_validate_rejects(field, value, code):
+    p = _cpu_problem(**{field: value})
+    assert _status(p) == code
+    assert len(m.lib().mla_last_error().decode()) > 0
+
+
+def test_decode_entry_points_fail_before_launch():
+    """Invalid arguments return an error from every entry point without
+    touching the device (this test runs without a GPU)."""
+    L = m.lib()
+    p = _cpu_problem(num_heads=200)
+    assert L.mla_decode_segments(ctypes.byref(p), 1, 1, 1, None) == m.MLA_ERR_UNSUPPORTED
+    assert L.mla_decode(ctypes.byref(p), None, 1, 1, 1, None, 0, None) == m.MLA_ERR_UNSUPPORTED
+    assert L.mla_merge_segments(1, 1, 1, 1, 2, 16, 0, 512, 16, None, 1, 1, 1, None) == m.MLA_ERR_INVALID_ARG
+    assert L.mla_merge_segments(1, 1, 1, 1, 2, 16, 4, 512, 16, None, 1, 99, 1, None) == m.MLA_ERR_UNSUPPORTED
+    p2 = _cpu_problem(num_segments=0)
+    p2.num_segments = 4
+    assert L.mla_decode(ctypes.byref(p2), None, 16, 1, 16, None, 0, None) == m.MLA_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op():
+    p = _cpu_problem(T=0, R=0)
+    L = m.lib()
+    assert L.mla_decode_segments(ctypes.byref(p), None, None, None, None) == m.MLA_OK
+    assert L.mla_merge_segments(None, None, None, None, 0, 16, 4, 512, 16, None, None, 1, None, None) == m.MLA_OK
+
+
+def test_sink_contract_wording():
+    with pytest.raises(ValueError, match="sinks must be float32"):
+        m.check_sinks(torch.zeros(16, dtype=torch.float64), 16)
+    with pytest.raises(ValueError, match=r"sinks must have shape \(16,\)"):
+        m.check_sinks(torch.zeros(8, dtype=torch.float32), 16)
+    with pytest.raises(ValueError, match="sinks must be contiguous"):
+        m.check_sinks(torch.zeros(32, dtype=torch.float32)[::2], 16)
+    m.check_sinks(torch.zeros(16, dtype=torch.float32), 16)
+
+
+def test_dtype_pair_mismatch_raises():
+    q = torch.zeros((1, 16, 576), dtype=torch.bfloat16)
+    kv = torch.zeros((2, 16, 576), dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError, match="must match"):
+        m.make_problem(q, kv, torch.zeros((1, 1), dtype=torch.int32), torch.ones(1, dtype=torch.int32),
+                       softmax_scale=0.1, max_seq_len=1)

@@ -1,0 +1,224 @@
+"""GPU parity of the HIP path against the fp64 oracle (run with -m gpu).
+
+Every call goes through the C ABI (ctypes binding); nothing here computes a
+result on the host except the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+from oracle import mla_oracle as orc
+
+from gpu_helpers import LSE_TOL, assert_close, out_tol, run_decode, run_segments, vmax
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import mla_paged_decode_02_amd as m
+    m.lib()  # the HIP library must load; no fallback exists
+
+
+def _print_case(name):
+    print(f"[case] {name}", flush=True)
+
+
+# ------------------------------------------------------------ tiny (page C1) --
+
+def test_tiny_fused_and_segmented():
+    w = mi.tiny()
+    _print_case(w.name)
+    ref_o, ref_l = orc.mla_decode(w)
+    out, lse = run_decode(w, num_segments=4)
+    assert_close(w, out, lse, ref_o, ref_l)
+    # bf16 output rounding on top
+    out_b, lse_b = run_decode(w, num_segments=4, out_dtype=torch.bfloat16)
+    assert_close(w, out_b, lse_b, ref_o, ref_l)
+    # two-call path: partials then merge
+    import mla_paged_decode_02_amd as m
+    so, sm, se, d = run_segments(w, 4, 16)
+    o2, l2 = m.merge_segments(torch.from_numpy(so).cuda(), torch.from_numpy(sm).cuda(),
+                              torch.from_numpy(se).cuda(), d["seq_lens"], 16,
+                              out_dtype=torch.float32)
+    assert_close(w, o2.cpu().numpy().astype(np.float64), l2.cpu().numpy().astype(np.float64),
+                 ref_o, ref_l)
+
+
+def test_tiny_partials_match_oracle_segments():
+    w = mi.tiny()
+    S, T = 4, 16
+    so, sm, se, _ = run_segments(w, S, T)
+    rso, rsm, rse, valid, _ = orc.mla_decode_segments(w, S, T)
+    vm = vmax(w)
+    for t in range(w.num_tokens):
+        for s in range(S):
+            if not valid[t, s]:
+                continue
+            # base-2 max: fp32 dot products of exact bf16 products
+            assert np.max(np.abs(sm[t, :, s] - rsm[t, :, s])) < 1e-4
+            assert np.max(np.abs(se[t, :, s] / rse[t, :, s] - 1)) < 1e-3
+            norm = so[t, :, s] / se[t, :, s][:, None]
+            rnorm = rso[t, :, s] / rse[t, :, s][:, None]
+            assert np.max(np.abs(norm - rnorm)) <= 1e-2 * vm
+
+
+# ------------------------------------------------ bit-exact partition check --
+
+def _bits_workload(seq_lens, block, dtype, H=16, qlens=None, causal=False, seed=0):
+    """q = 0 and V[d] = bit (d % 16) of (logical position + 1000 * request):
+    every visible position has p = 1, so a segment's partials are integers."""
+    w = mi.make_workload(name="bits", seq_lens=seq_lens, num_heads=H, block_size=block,
+                         dtype=dtype, qlens=qlens, causal=causal, seed=seed)
+    one = 0x3F80 if dtype == "bf16" else 0x38
+    flat = w.kv_cache.reshape(-1, 576)
+    for r, n in enumerate(w.seq_lens):
+        for j in range(int(n)):
+            code = (j + 1000 * r)
+            bits = [(code >> (d % 16)) & 1 for d in range(576)]
+            flat[orc.cache_row_index(w.block_table[r], j, block)] = np.array(bits) * one
+    w.q[:] = 0
+    w.kv_scale = None
+    w.q_scale = None
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("lens,block,tile,S", [
+    ([17, 100, 257, 1], 16, 16, 4),
+    ([17, 100, 257, 1], 16, 4, 7),
+    ([1000, 63, 64, 65], 64, 64, 3),
+    ([4097, 31, 2048], 256, 128, 5),
+    ([333, 700], 96, 32, 9),
+    ([50, 129], 1, 1, 64),
+])
+def test_partition_bit_exact(dtype, lens, block, tile, S):
+    _print_case(f"bits {dtype} lens={lens} block={block} tile={tile} S={S}")
+    w = _bits_workload(lens, block, dtype)
+    so, sm, se, _ = run_segments(w, S, tile)
+    for r, n in enumerate(lens):
+        bounds = orc.segment_bounds(n, S, tile)
+        for s, (a, b) in enumerate(bounds):
+            assert np.all(sm[r, :, s] == 0.0), (r, s)
+            assert np.all(se[r, :, s] == b - a), (r, s, se[r, 0, s], b - a)
+            for d in range(16):
+                cnt = sum(((j + 1000 * r) >> d) & 1 for j in range(a, b))
+                assert np.all(so[r, :, s, d] == cnt), (r, s, d)
+            # dims repeat with period 16
+            assert np.array_equal(so[r, :, s, 16:32], so[r, :, s, 0:16])
+
+
+def test_partition_bit_exact_causal():
+    lens, qlens = [40, 200, 5], [4, 3, 2]
+    w = _bits_workload(lens, 16, "bf16", H=5, qlens=qlens, causal=True)
+    S, tile = 3, 16
+    so, sm, se, _ = run_segments(w, S, tile)
+    for r, n in enumerate(lens):
+        t0 = int(w.qo_indptr[r])
+        for i in range(qlens[r]):
+            vis = orc.visible_len(n, qlens[r], i, True)
+            for s, (a, b) in enumerate(orc.segment_bounds(n, S, tile)):
+                cnt = max(0, min(b, vis) - a)
+                if cnt == 0:
+                    assert np.all(np.isneginf(sm[t0 + i, :, s])) and np.all(se[t0 + i, :, s] == 0)
+                    assert np.all(so[t0 + i, :, s] == 0)
+                else:
+                    assert np.all(sm[t0 + i, :, s] == 0) and np.all(se[t0 + i, :, s] == cnt)
+
+
+# ---------------------------------------------------------- parity sweep -----
+
+SWEEP = [
+    # (dtype, H, block, lens, qlens, causal, sinks, S)
+    ("bf16", 16, 64, [3000, 1, 64, 700], None, False, False, 5),
+    ("bf16", 1, 16, [300, 17], None, False, True, 3),
+    ("bf16", 3, 256, [1500, 129], None, False, True, 2),
+    ("bf16", 20, 64, [999, 64], None, False, False, 4),
+    ("bf16", 48, 64, [1200, 31], None, False, True, 3),
+    ("bf16", 64, 32, [777, 2048], None, False, False, 2),
+    ("bf16", 96, 64, [600, 65], None, False, True, 2),
+    ("bf16", 128, 256, [1300, 200], None, False, False, 3),
+    ("bf16", 16, 64, [500, 2000, 7, 64], [1, 2, 3, 4], True, True, 3),
+    ("fp8_e4m3", 16, 64, [3000, 2, 640], None, False, False, 5),
+    ("fp8_e4m3", 48, 64, [1600, 100], None, False, True, 3),
+    ("fp8_e4m3", 64, 64, [1111, 4096], None, False, False, 2),
+    ("fp8_e4m3", 96, 64, [900, 44, 3000], [1, 4, 2], True, True, 3),
+    ("fp8_e4m3", 128, 128, [1024, 3], None, False, False, 2),
+    ("fp8_e4m3", 7, 8, [170, 33], [3, 1], True, True, 4),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"{c[0]}-H{c[1]}-blk{c[2]}-q{c[4] is not None}-S{c[7]}")
+def test_parity_sweep(case):
+    dtype, H, block, lens, qlens, causal, sinks, S = case
+    _print_case(str(case))
+    w = mi.make_workload(name="sweep", seq_lens=lens, num_heads=H, block_size=block, dtype=dtype,
+                         qlens=qlens, causal=causal, sinks=sinks,
+                         seed=1000 * H + block + (7 if dtype == "bf16" else 0))
+    ref_o, ref_l = orc.mla_decode(w)
+    out, lse = run_decode(w, num_segments=S)
+    assert_close(w, out, lse, ref_o, ref_l)
+
+
+def test_planner_choice_and_empty_requests():
+    """num_segments = 0 (planner) and requests of length 0, with sinks."""
+    w = mi.make_workload(name="empty", seq_lens=[0, 500, 0, 64], num_heads=16, block_size=64,
+                         dtype="bf16", sinks=True, seed=31)
+    ref_o, ref_l = orc.mla_decode(w)
+    out, lse = run_decode(w, num_segments=0)
+    assert_close(w, out, lse, ref_o, ref_l)
+    assert np.all(out[0] == 0) and np.allclose(lse[0], w.sinks, atol=0, rtol=0)
+    out2, lse2 = run_decode(w, num_segments=0, sinks=False)
+    assert np.all(out2[0] == 0) and np.all(np.isneginf(lse2[0]))
+
+
+def test_head_count_independent_bits():
+    """Heads are independent: the first 16 heads of an H=48 batch give the
+    same bits as an H=16 batch with those heads (no head folding)."""
+    w48 = mi.make_workload(name="h48", seq_lens=[2000, 300], num_heads=48, block_size=64,
+                           dtype="fp8_e4m3", seed=41)
+    w16 = mi.with_(w48, q=np.ascontiguousarray(w48.q[:, :16]), num_heads=16)
+    o48, l48 = run_decode(w48, num_segments=3)
+    o16, l16 = run_decode(w16, num_segments=3)
+    assert np.array_equal(o48[:, :16], o16) and np.array_equal(l48[:, :16], l16)
+
+
+def test_strided_views():
+    """q as a head-strided view, block table read through a column stride."""
+    import mla_paged_decode_02_amd as m
+    w = mi.make_workload(name="strided", seq_lens=[900, 130], num_heads=8, block_size=32,
+                         dtype="bf16", seed=51)
+    ref_o, ref_l = orc.mla_decode(w)
+    d = mi.to_torch(w, "cuda")
+    big = torch.zeros((w.num_tokens, w.num_heads, 640), dtype=torch.bfloat16, device="cuda")
+    big[:, :, :576] = d["q"]
+    qv = big[:, :, :576]
+    btT = d["block_table"].t().contiguous().t()  # column stride != 1
+    assert btT.stride(1) != 1
+    out, lse = m.decode(qv, d["kv_cache"], btT, d["seq_lens"], softmax_scale=w.softmax_scale,
+                        max_seq_len=w.max_seq_len, num_segments=3, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                 ref_o, ref_l)
+
+
+@pytest.mark.parametrize("odt", [torch.bfloat16, torch.float16, torch.float32])
+def test_output_dtypes(odt):
+    w = mi.make_workload(name="odt", seq_lens=[700, 40], num_heads=16, block_size=64, dtype="bf16",
+                         seed=61)
+    ref_o, ref_l = orc.mla_decode(w)
+    out, lse = run_decode(w, num_segments=2, out_dtype=odt)
+    assert_close(w, out, lse, ref_o, ref_l)
+
+
+def test_poison_never_read():
+    """Pages past a request's end and page tails hold NaN: outputs stay finite."""
+    w = mi.make_workload(name="poison", seq_lens=[65, 1, 127, 64], num_heads=16, block_size=64,
+                         dtype="bf16", seed=71, extra_bt_cols=3)
+    out, lse = run_decode(w, num_segments=2)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
