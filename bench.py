@@ -50,7 +50,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-reqs", type=int, default=4)
     ap.add_argument("--num-segments", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(torch, reps=5):
+    """A plain copy of known size: the HBM counters read for it calibrate the
+    segment kernel's FETCH_SIZE / WRITE_SIZE per launch."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "reps": reps}), flush=True)
 
 
 def build_inputs(name, torch, mi):
@@ -165,8 +180,11 @@ def main():
     import mla_inputs as mi
     import mla_paged_decode_02_amd as m
 
-    m.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    m.lib()
     t0 = time.time()
     w, res, roof = time_workload(args.workload, args, torch, m, mi, want_roofline=True)
     extra = []

@@ -10,7 +10,13 @@ namespace mla {
 
 constexpr int kHeadDim = 576;
 constexpr int kKvRank = 512;
-constexpr int kTileTokens = 32;  // tokens per LDS tile of the segment kernel
+// Tokens per LDS tile of the segment kernel: 16 for bf16 with one wave per
+// workgroup (so four workgroups share a CU's LDS), else 32.
+constexpr int tile_tokens(bool fp8, int waves) { return (!fp8 && waves == 1) ? 16 : 32; }
+// LDS ring bytes per workgroup for a given wave count.
+constexpr int ring_bytes(int waves) { return waves == 1 ? 36864 : waves == 2 ? 73728 : 147456; }
+// Workgroups of that size one CU holds at once (LDS-bound).
+constexpr int wgs_per_cu(int waves) { return 147456 / ring_bytes(waves); }
 
 struct SegmentLaunch {
   // query
@@ -57,7 +63,7 @@ struct SegmentShape {
   int waves;          // waves per workgroup (1..4)
   int rows_per_wave;  // 16-row groups per wave (1 or 2)
   int chunks;         // row chunks per (request, segment)
-  bool contig;  // TILE >= 32: a 32-token LDS tile is one contiguous run of rows
+  bool contig;        // TILE >= tile tokens: an LDS tile is one contiguous run of rows
 };
 
 SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile);

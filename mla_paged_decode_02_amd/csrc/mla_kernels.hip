@@ -46,6 +46,11 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
+// Cache policy of the cache-row stream: non-temporal (each row is read once
+// per segment), which measured ~10% faster than the default policy.
+constexpr int kStreamPolicy = 2;
 // The softmax reference max moves only past this many base-2 units (p <= 2^8).
 constexpr float kLazy = 8.0f;
 
@@ -147,21 +152,23 @@ __device__ __forceinline__ T lds_load(const char* base, int off) {
 }
 
 // NW waves x RG row groups of 16 rows per workgroup.
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG>
+// TT tokens per LDS tile (16 or 32; fp8 always uses 32).
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT>
 __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
   using F = KvFmt<FP8>;
+  static_assert(TT == 32 || (TT == 16 && !FP8), "tile shape");
+  constexpr int kNB = TT / 16;                         // 16-token blocks per tile
   constexpr int kRowBytes = F::kRowBytes;
-  constexpr int kVRegion = kTileTokens * F::kVPitch;
-  constexpr int kTileBytes = kTileTokens * kRowBytes;  // 36864 (bf16) / 18432 (fp8)
+  constexpr int kVRegion = TT * F::kVPitch;
+  constexpr int kTileBytes = TT * kRowBytes;           // bf16 36864 / 18432, fp8 18432
   constexpr int kRowsPerV = 1024 / F::kVPitch;         // rows per V-region DMA instruction
-  constexpr int kNIV = kTileTokens / kRowsPerV;        // V-region DMA instructions
+  constexpr int kNIV = TT / kRowsPerV;                 // V-region DMA instructions
   constexpr int kNI = kTileBytes / 1024;               // all DMA instructions per tile
-  constexpr int kNIw = kNI / NW;                       // per wave, lower bound
-  constexpr int kNIwMax = (kNI + NW - 1) / NW;
+  constexpr int kNIw = kNIV / NW + (kNI - kNIV) / NW;   // per wave, lower bound
   constexpr int kRowsWG = 16 * RG * NW;
   static_assert(kTileBytes % 1024 == 0, "tile must be whole DMA instructions");
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][kTileBytes];
-  __shared__ int phys_rows[CONTIG ? 1 : kTileTokens];
+  __shared__ int phys_rows[CONTIG ? 1 : TT];
 
   const int s = blockIdx.x;
   const int r = blockIdx.y;
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
   const int last_row = min(row0 + kRowsWG, M) - 1;
   const int lim_wg = p.causal ? (L - qlen + last_row / H + 1) : L;
   const int eff_end = min(min(seg_end, lim_wg), cap);
-  const int ntiles = eff_end > seg_start ? cdiv(eff_end - seg_start, kTileTokens) : 0;
+  const int ntiles = eff_end > seg_start ? cdiv(eff_end - seg_start, TT) : 0;
 
   // ---- this lane's query rows (one per row group) ----
   int ti[RG], hh[RG], end_row[RG];
@@ -239,23 +246,72 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
   wait_vmcnt<0>();  // q is in registers before the DMA stream starts
 
   // ---- DMA of one 32-token tile into ring slot b ----
-  // Instruction kk < kNIV fills V-region row(s) kk*kRowsPerV.., later ones the
-  // rope region; lane lambda writes LDS byte 16*lambda of its instruction's
-  // 1 KiB and loads the logical chunk that the swizzle stores there.
+  // V region: instruction i of this wave fills V row index vi = wave + NW*i
+  // (bf16: tile row vi, 64 chunks; fp8: rows 2vi and 2vi+1, 32 chunks each).
+  // Rope region: bf16 4 instructions of 8 rows, fp8 2 of 16 rows.  Lane
+  // lambda writes LDS byte 16*lambda of its instruction's 1 KiB and loads the
+  // logical chunk the swizzle stores there.  Rows at or past the tile's valid
+  // count load tile row 0 instead (finite data that the softmax masks).
+  constexpr int kNIR = kNI - kNIV;  // rope instructions per tile
+  static_assert(kNIV % NW == 0, "V rows split evenly over the waves");
+  constexpr int kVPerWave = kNIV / NW;
+  constexpr int kRopePerWaveMax = (kNIR + NW - 1) / NW;
+  constexpr int kRowsPerRope = 64 / F::kRopeChunks;
+  const int lane16 = 16 * lane;
+  const int v_half = lane / F::kVChunks;  // fp8: which of the instruction's two rows
+  const int v_cpos = lane % F::kVChunks;
+  const int rope_row_in = lane / F::kRopeChunks;
+  const int rope_cpos = lane % F::kRopeChunks;
+
   auto issue_tile = [&](int k, int b) {
-    const int tile_start = seg_start + k * kTileTokens;
-    const int nvalid = min(kTileTokens, eff_end - tile_start);
-    const char* base = nullptr;
+    const int tile_start = seg_start + k * TT;
+    const int nvalid = min(TT, eff_end - tile_start);
+    char* ldst = &lds[b][0];
     if constexpr (CONTIG) {
+      // Uniform address, read-only table: a scalar load through the constant
+      // address space, so no vector-memory wait drains the DMA stream.
       const int blk_i = tile_start / p.block_size;
-      int blk = p.block_table[(int64_t)r * p.bt_stride_row + (int64_t)blk_i * p.bt_stride_col];
+      int blk = ((const __attribute__((address_space(4))) int*)p.block_table)
+          [(int64_t)r * p.bt_stride_row + (int64_t)blk_i * p.bt_stride_col];
       if (blk < 0 || blk >= p.num_blocks) { blk = 0; bad = true; }
       const int64_t phys0 = (int64_t)blk * p.block_size + (tile_start - blk_i * p.block_size);
-      base = p.kv + phys0 * kRowBytes;
+      // Buffer descriptor over the tile's 32 rows (a guard: no offset below
+      // leaves them); per instruction a scalar row offset plus one 32-bit
+      // per-lane chunk offset.
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.kv + phys0 * kRowBytes), 0, TT * kRowBytes, kBufferFlags);
+      const int key16 = opaque(lane16);
+#pragma unroll
+      for (int i = 0; i < kVPerWave; ++i) {
+        const int vi = wave + NW * i;
+        int voff, soff;
+        if constexpr (!FP8) {
+          soff = (vi < nvalid ? vi : 0) * kRowBytes;
+          voff = key16 ^ (16 * swz_v(vi));
+        } else {
+          // rows 2vi (lanes 0-31) and 2vi+1 (lanes 32-63); swz_v(2vi+1) = swz_v(2vi) ^ 2
+          const int row = 2 * vi + v_half;
+          soff = 0;
+          voff = (row < nvalid ? row * kRowBytes : 0) +
+                 ((16 * v_cpos) ^ (32 * v_half) ^ (16 * swz_v(2 * vi)));
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(ldst + vi * 1024), 16, voff, soff, 0, kStreamPolicy);
+      }
+#pragma unroll
+      for (int i = 0; i < kRopePerWaveMax; ++i) {
+        const int ri = wave + NW * i;
+        if (ri < kNIR) {
+          const int row = ri * kRowsPerRope + rope_row_in;
+          const int rr = row < nvalid ? row : 0;
+          const int voff = rr * kRowBytes + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(ldst + (kNIV + ri) * 1024), 16, voff, 0, 0, kStreamPolicy);
+        }
+      }
     } else {
-      // Rows of a tile span several pages: thread j < 32 resolves tile row j.
+      // Rows of a tile span several pages: thread j < 32 resolves tile row j
+      // (rows past the valid count resolve to tile row 0).
       __syncthreads();  // previous readers of phys_rows are done
-      if (threadIdx.x < kTileTokens) {
+      if (threadIdx.x < TT) {
         const int j = tile_start + ((int)threadIdx.x < nvalid ? (int)threadIdx.x : 0);
         const int blk_i = j / p.block_size;
         const int blk = p.block_table[(int64_t)r * p.bt_stride_row + (int64_t)blk_i * p.bt_stride_col];
@@ -263,33 +319,31 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
             (blk < 0 || blk >= p.num_blocks) ? -1 : blk * p.block_size + (j - blk_i * p.block_size);
       }
       __syncthreads();
-    }
-    const int ln = opaque(lane);
+      auto row_ptr = [&](int row) -> const char* {
+        int pr = phys_rows[row];
+        if (pr < 0) { pr = 0; bad = true; }
+        return p.kv + (int64_t)pr * kRowBytes;
+      };
 #pragma unroll
-    for (int i = 0; i < kNIwMax; ++i) {
-      const int kk = i * NW + wave;
-      if (kk < kNI) {
-        int trow, gbyte;
-        if (kk < kNIV) {
-          trow = kk * kRowsPerV + ln / F::kVChunks;
-          const int cpos = ln % F::kVChunks;
-          gbyte = 16 * (cpos ^ swz_v(trow));
-        } else {
-          constexpr int kRowsPerRope = 64 / F::kRopeChunks;
-          trow = (kk - kNIV) * kRowsPerRope + ln / F::kRopeChunks;
-          const int cpos = ln % F::kRopeChunks;
-          gbyte = kKvRank * (FP8 ? 1 : 2) + 16 * (cpos ^ F::swz_r(trow));
-        }
-        const int rr = trow < nvalid ? trow : 0;
+      for (int i = 0; i < kVPerWave; ++i) {
+        const int vi = wave + NW * i;
         const char* src;
-        if constexpr (CONTIG) {
-          src = base + rr * kRowBytes + gbyte;
+        if constexpr (!FP8) {
+          src = row_ptr(vi) + (unsigned)(lane16 ^ (16 * swz_v(vi)));
         } else {
-          int pr = phys_rows[rr];
-          if (pr < 0) { pr = 0; bad = true; }
-          src = p.kv + (int64_t)pr * kRowBytes + gbyte;
+          const int row = 2 * vi + v_half;
+          src = row_ptr(row) + 16 * (v_cpos ^ swz_v(row));
         }
-        __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)&lds[b][kk * 1024], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(ldst + vi * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kRopePerWaveMax; ++i) {
+        const int ri = wave + NW * i;
+        if (ri < kNIR) {
+          const int row = ri * kRowsPerRope + rope_row_in;
+          const char* src = row_ptr(row) + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
+          __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(ldst + (kNIV + ri) * 1024), 16, 0, 0);
+        }
       }
     }
   };
@@ -356,7 +410,7 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
     if (!wave_has_rows) continue;
 
     const char* buf = lds[k % NBUF];
-    const int tile_start = seg_start + k * kTileTokens;
+    const int tile_start = seg_start + k * TT;
     int kvb[2], kvx[2], krb[2], krx[2], vtb[2], vtx[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -365,12 +419,13 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
       vtb[b] = opaque(vt_base[b]); vtx[b] = opaque(vt_x[b]);
     }
 
-    // S^T = K . Q^T for the two 16-token blocks: 36 (chunk, block) steps,
-    // operands prefetched kPF steps ahead.
+    // S^T = K . Q^T for the tile's 16-token blocks: 18 * kNB (chunk, block)
+    // steps, operands prefetched kPF steps ahead.
     typedef typename std::conditional<FP8, long, bf16x8>::type KOp;
     constexpr int kPF = 4;
+    constexpr int kSteps = 18 * kNB;
     auto k_off = [&](int st) {
-      const int c = st >> 1, b = st & 1;
+      const int c = st / kNB, b = st % kNB;
       if (c < 16) {
         const int lc = FP8 ? (2 * c) : (4 * c);  // logical chunk without the lane part
         return kvb[b] + 16 * (lc ^ kvx[b]);
@@ -385,10 +440,10 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
 #pragma unroll
     for (int i = 0; i < kPF; ++i) kop[i] = lds_load<KOp>(buf, k_off(i));
 #pragma unroll
-    for (int st = 0; st < 36; ++st) {
+    for (int st = 0; st < kSteps; ++st) {
       const KOp cur = kop[st % kPF];
-      if (st + kPF < 36) kop[st % kPF] = lds_load<KOp>(buf, k_off(st + kPF));
-      const int c = st >> 1, b = st & 1;
+      if (st + kPF < kSteps) kop[st % kPF] = lds_load<KOp>(buf, k_off(st + kPF));
+      const int c = st / kNB, b = st % kNB;
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         if constexpr (FP8)
@@ -402,15 +457,16 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
     // Base-2 online softmax per row over this tile.  The reference max m_run
     // only moves when the tile max exceeds it by more than kLazy (so p <= 2^kLazy);
     // m_true tracks the exact max and the end rescales to it once.
-    bf16x8 pb[RG];
+    typedef typename std::conditional<kNB == 2, bf16x8, i16x4>::type POp;
+    POp pb[RG];
     bool rescale = false;
     float alpha[RG];
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
-      float x[8];
+      float x[4 * kNB];
       float mloc = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4 * kNB; ++i) {
         // score slot i: block i/4, A-row 4g + i%4
         const int tok = tile_start + 16 * (i >> 2) + 4 * g + (i & 3);
         const float v = (tok < end_row[q]) ? sblk[q][i >> 2][i & 3] * sl2 : -INFINITY;
@@ -421,15 +477,15 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
       m_true[q] = fmaxf(m_true[q], mloc);
       const float m_new = (mloc > m_run[q] + kLazy) ? mloc : m_run[q];
       alpha[q] = 1.f;
-      float pv[8];
+      float pv[4 * kNB];
       if (m_new == -INFINITY) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = 0.f;
+        for (int i = 0; i < 4 * kNB; ++i) pv[i] = 0.f;
       } else {
         alpha[q] = __builtin_amdgcn_exp2f(m_run[q] - m_new);
         float psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4 * kNB; ++i) {
           pv[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
           psum += pv[i];
         }
@@ -437,7 +493,12 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
       }
       m_run[q] = m_new;
       rescale |= alpha[q] != 1.f;
-      pb[q] = to_bf16x8(pv);
+      if constexpr (kNB == 2) {
+        pb[q] = to_bf16x8(pv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[q][i] = __builtin_bit_cast(short, (__bf16)pv[i]);
+      }
     }
     if (__ballot(rescale)) {
 #pragma unroll
@@ -448,9 +509,13 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
     __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T . P^T over 32 dim blocks of 16, operands prefetched kPF ahead.
-    typedef typename std::conditional<FP8, i32x2, bf16x8>::type VRaw;
+    typedef typename std::conditional<FP8, i32x2, typename std::conditional<kNB == 2, bf16x8, i16x4>::type>::type VRaw;
     auto v_load = [&](int db) -> VRaw {
-      if constexpr (FP8) {
+      if constexpr (kNB == 1) {
+        // one 16-token block: k-slots 4g..4g+3 from a single transpose read
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(buf + vtb[0] + 16 * ((2 * db) ^ vtx[0])));
+      } else if constexpr (FP8) {
         // logical chunk db, half j
         return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (LDS_AS i32x2*)(buf + vtb[0] + 16 * (db ^ vtx[0])));
@@ -470,12 +535,18 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
     for (int db = 0; db < 32; ++db) {
       const VRaw cur = vop[db % kPF];
       if (db + kPF < 32) vop[db % kPF] = v_load(db + kPF);
-      bf16x8 va;
-      if constexpr (FP8) va = fp8x8_to_bf16x8(__builtin_bit_cast(u32x2, cur));
-      else va = cur;
+      if constexpr (kNB == 1) {
 #pragma unroll
-      for (int q = 0; q < RG; ++q)
-        acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[q], acc[q][db], 0, 0, 0);
+        for (int q = 0; q < RG; ++q)
+          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur, pb[q], acc[q][db], 0, 0, 0);
+      } else {
+        bf16x8 va;
+        if constexpr (FP8) va = fp8x8_to_bf16x8(__builtin_bit_cast(u32x2, cur));
+        else va = cur;
+#pragma unroll
+        for (int q = 0; q < RG; ++q)
+          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[q], acc[q][db], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -517,12 +588,17 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
   return (unsigned short)(u >> 16);
 }
 
+// One wave per (token, head) row; lane covers dims [8*lane, 8*lane+8).  The
+// valid segments' statistics are read one per lane (up to 64 at a time), the
+// weights 2^(m_s - M) broadcast from the owning lane, and the partial rows
+// streamed with several loads in flight.
 template <int OUT>  // 0 bf16, 1 fp16, 2 fp32
 __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
-  const int t = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (h >= p.num_heads) return;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)p.num_tokens * p.num_heads) return;
+  const int t = (int)(row / p.num_heads);
+  const int h = (int)(row - (int64_t)t * p.num_heads);
   const int S = p.num_segments;
 
   int L;
@@ -544,39 +620,66 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
     const int span = cdiv(L, S * p.tile) * p.tile;
     nv = min(S, cdiv(L, span));
   }
-  const int64_t base = ((int64_t)t * p.num_heads + h) * S;
+  const int64_t base = row * S;
 
-  // global max and error flag over the valid segments
+  // Pass 1: global max M, error flag, and L = sum l_s 2^(m_s - M).
   float M = -INFINITY;
   bool nan_seen = false;
-  for (int s = lane; s < nv; s += 64) {
-    const float m = p.seg_max[base + s];
+  for (int s0 = 0; s0 < nv; s0 += 64) {
+    const int s = s0 + lane;
+    const float m = s < nv ? p.seg_max[base + s] : -INFINITY;
     nan_seen |= (m != m);
     M = fmaxf(M, m);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   nan_seen = __ballot(nan_seen) != 0;
-
-  float Lsum = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const bool has = M > -INFINITY;
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float Lsum = 0.f;
   if (has) {
-    for (int s = lane; s < nv; s += 64) {
-      const float m = p.seg_max[base + s];
-      if (m > -INFINITY) Lsum += p.seg_sum[base + s] * exp2f(m - M);
+    for (int s0 = 0; s0 < nv; s0 += 64) {
+      const int s = s0 + lane;
+      float wgt = 0.f;
+      if (s < nv) {
+        const float m = p.seg_max[base + s];
+        wgt = (m > -INFINITY) ? exp2f(m - M) : 0.f;
+        Lsum += p.seg_sum[base + s] * wgt;
+      }
+      const int cnt = min(64, nv - s0);
+      const float* src = p.seg_out + (base + s0) * kKvRank + 8 * lane;
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[2 * u] = *(const f32x4*)(src + (j + u) * kKvRank);
+          v[2 * u + 1] = *(const f32x4*)(src + (j + u) * kKvRank + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float wu = __shfl(wgt, j + u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[e] += wu * v[2 * u][e];
+            acc[4 + e] += wu * v[2 * u + 1][e];
+          }
+        }
+      }
+      for (; j < cnt; ++j) {
+        const f32x4 a = *(const f32x4*)(src + j * kKvRank);
+        const f32x4 b = *(const f32x4*)(src + j * kKvRank + 4);
+        const float wu = __shfl(wgt, j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += wu * a[e];
+          acc[4 + e] += wu * b[e];
+        }
+      }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) Lsum += __shfl_xor(Lsum, o);
-    for (int s = 0; s < nv; ++s) {
-      const float m = p.seg_max[base + s];
-      if (!(m > -INFINITY)) continue;
-      const float w = exp2f(m - M);
-      const f32x4* src = (const f32x4*)(p.seg_out + (base + s) * kKvRank + 8 * lane);
-      const f32x4 a = src[0], b = src[1];
-      acc[0] += w * a[0]; acc[1] += w * a[1]; acc[2] += w * a[2]; acc[3] += w * a[3];
-      acc[4] += w * b[0]; acc[5] += w * b[1]; acc[6] += w * b[2]; acc[7] += w * b[3];
-    }
   }
   float lse;
   float scale;
@@ -599,7 +702,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = has ? acc[i] * scale : (nan_seen ? scale : 0.f);
 
-  const int64_t orow = ((int64_t)t * p.num_heads + h) * kKvRank + 8 * lane;
+  const int64_t orow = row * kKvRank + 8 * lane;
   if constexpr (OUT == 0) {
     u32x4 v;
 #pragma unroll
@@ -619,30 +722,28 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
     dst[0] = f32x4{o[0], o[1], o[2], o[3]};
     dst[1] = f32x4{o[4], o[5], o[6], o[7]};
   }
-  if (lane == 0) p.lse[(int64_t)t * p.num_heads + h] = lse;
+  if (lane == 0) p.lse[row] = lse;
 }
 
 template <bool FP8, int NW, int RG, bool CONTIG>
 hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
-  // LDS ring: 72 KiB for 1-2 waves (two workgroups per CU), 144 KiB for 3-4
-  // waves (one workgroup per CU).
-  constexpr int kTileBytes = kTileTokens * (FP8 ? 576 : 1152);
-  constexpr int kRing = (NW <= 2 ? 73728 : 147456) / kTileBytes;
+  // LDS ring per workgroup: 36 KiB with 1 wave (four workgroups per CU; bf16
+  // uses 16-token tiles there), 72 KiB with 2 waves (two per CU), 144 KiB
+  // with 4 waves (one per CU).
+  constexpr int kTT = tile_tokens(FP8, NW);
+  constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
+  constexpr int kRing = ring_bytes(NW) / kTileBytes;
   dim3 grid(a.num_segments, a.num_reqs, chunks);
-  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG>), grid, dim3(64 * NW), 0, stream, a);
+  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG, kTT>), grid, dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool FP8, bool CONTIG>
 hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, hipStream_t stream) {
-  if (sh.rows_per_wave == 2) {
-    if (sh.waves == 3) return launch_seg<FP8, 3, 2, CONTIG>(a, sh.chunks, stream);
-    return launch_seg<FP8, 4, 2, CONTIG>(a, sh.chunks, stream);
-  }
+  if (sh.rows_per_wave == 2) return launch_seg<FP8, 4, 2, CONTIG>(a, sh.chunks, stream);
   switch (sh.waves) {
     case 1: return launch_seg<FP8, 1, 1, CONTIG>(a, sh.chunks, stream);
     case 2: return launch_seg<FP8, 2, 1, CONTIG>(a, sh.chunks, stream);
-    case 3: return launch_seg<FP8, 3, 1, CONTIG>(a, sh.chunks, stream);
     default: return launch_seg<FP8, 4, 1, CONTIG>(a, sh.chunks, stream);
   }
 }
@@ -656,13 +757,11 @@ SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
   // groups of 16 rows -> (waves, row groups per wave)
   if (groups <= 1)      { sh.waves = 1; sh.rows_per_wave = 1; }
   else if (groups == 2) { sh.waves = 2; sh.rows_per_wave = 1; }
-  else if (groups == 3) { sh.waves = 3; sh.rows_per_wave = 1; }
-  else if (groups == 4) { sh.waves = 4; sh.rows_per_wave = 1; }
-  else if (groups <= 6) { sh.waves = 3; sh.rows_per_wave = 2; }
+  else if (groups <= 4) { sh.waves = 4; sh.rows_per_wave = 1; }
   else                  { sh.waves = 4; sh.rows_per_wave = 2; }
   const int per_wg = sh.waves * sh.rows_per_wave;
   sh.chunks = (groups + per_wg - 1) / per_wg;
-  sh.contig = tile >= kTileTokens;
+  sh.contig = tile >= tile_tokens(fp8, sh.waves);
   return sh;
 }
 
@@ -674,7 +773,8 @@ hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, hipSt
 }
 
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
-  dim3 grid(a.num_tokens, (a.num_heads + 3) / 4);
+  const int64_t rows = (int64_t)a.num_tokens * a.num_heads;
+  dim3 grid((unsigned)((rows + 3) / 4));
   switch (a.out_dtype) {
     case 0: hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, a); break;
     case 1: hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, stream, a); break;
