@@ -33,6 +33,7 @@ HBM_PEAK_GBS = 8000.0
 WORKLOADS = {
     # name: (num_heads, dtype, block, seed)
     "bs52_ctx16k_h16_bf16_blk64": (16, "bf16", 64, 2),
+    "bs52_ctx16k_h16_fp8_blk64": (16, "fp8_e4m3", 64, 3),
     "bs52_ctx16k_h48_fp8_blk64": (48, "fp8_e4m3", 64, 3),
     "bs52_ctx16k_h64_fp8_blk64": (64, "fp8_e4m3", 64, 3),
     "bs52_ctx16k_h128_bf16_blk256": (128, "bf16", 256, 4),
@@ -84,15 +85,13 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     esz = 2 if w.kv_dtype == "bf16" else 1
     kv_bytes = w.kv_bytes_touched()
     calls = [mi.call_args(w, d) for d in ds]
-    p = m.make_problem(**calls[0], num_segments=args.num_segments)
-    S = m.resolve_num_segments(p)
-    ws = torch.empty(m.workspace_bytes(p), dtype=torch.uint8, device="cuda")
-    out = torch.empty((w.num_tokens, w.num_heads, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((w.num_tokens, w.num_heads), dtype=torch.float32, device="cuda")
+    # One prepared call per cache copy: each step is a single C call.
+    decs = [m.Decoder(**c, num_segments=args.num_segments, out_dtype=torch.bfloat16) for c in calls]
+    S = decs[0].num_segments
     stream = torch.cuda.current_stream()
 
     def step(i):
-        m.decode(**calls[i & 1], num_segments=S, out=out, lse=lse, workspace=ws, stream=stream)
+        decs[i & 1].run(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -129,6 +128,22 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     e1.record(stream)
     torch.cuda.synchronize()
     seg_ms = e0.elapsed_time(e1) / args.steps
+    # Merge kernel alone on the same partials.
+    part_lens = ds[0]["seq_lens"]
+    mo = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    ml = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    tile = w.tile_size or m.tile_size_for_block(w.block_size)
+    for i in range(args.warmup):
+        m.merge_segments(so, sm, se, part_lens, tile, out=mo, lse=ml, stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        m.merge_segments(so, sm, se, part_lens, tile, out=mo, lse=ml, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    merge_ms = e0.elapsed_time(e1) / args.steps
+    res["merge_kernel_us"] = merge_ms * 1e3
+
     # Algorithmic bytes of one segment-kernel launch: every cache row once,
     # q once, the fp32 partials of every valid segment written once.
     import mla_paged_decode_02_amd as mm
@@ -143,7 +158,6 @@ def time_workload(name, args, torch, m, mi, want_roofline):
             "kernel": "segment_kernel", "kernel_us": round(seg_ms * 1e3, 2),
             "algorithmic_bytes": alg}
     res["segment_kernel_us"] = seg_ms * 1e3
-    res["merge_and_launch_us"] = (ms - seg_ms) * 1e3
     return w, res, roof
 
 
@@ -215,6 +229,8 @@ def main():
                    "num_segments": res["num_segments"], "parallelism": "single GPU"},
         "frac_of_hbm_peak": round(res["frac_of_hbm_peak"], 4),
         "roofline": roof,
+        "segment_kernel_us": round(res.get("segment_kernel_us", 0.0), 2),
+        "merge_kernel_us": round(res.get("merge_kernel_us", 0.0), 2),
         "cpu_baseline": cpu,
         "extra": extra,
         "wall_s": round(time.time() - t0, 1),

@@ -322,3 +322,37 @@ def decode(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_
                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _stream(stream)))
     return out, lse
+
+
+class Decoder:
+    """A prepared ``mla_decode`` call for a fixed batch layout.
+
+    The descriptor, segment count, workspace and outputs are set up once; each
+    ``run()`` is one C call (no per-call Python argument processing), which is
+    what a serving loop re-issues every step.  The tensors passed here must stay
+    alive and keep their addresses; their contents may change between runs.
+    """
+
+    def __init__(self, q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_len: int,
+                 qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
+                 tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0,
+                 out_dtype=torch.bfloat16):
+        self.p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
+                              max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen,
+                              causal=causal, q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
+                              num_segments=num_segments, sum_seq_lens=sum_seq_lens)
+        check_sinks(sinks, q.shape[1])
+        self.num_segments = resolve_num_segments(self.p)
+        self.p.num_segments = self.num_segments
+        T, H = q.shape[0], q.shape[1]
+        self.out = torch.empty((T, H, KV_LORA_RANK), dtype=out_dtype, device=q.device)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+        self.workspace = torch.empty(max(workspace_bytes(self.p), 256), dtype=torch.uint8, device=q.device)
+        self._keep = (q, kv_cache, block_table, seq_lens, qo_indptr, q_scale, kv_scale, sinks)
+        self._fn = lib().mla_decode
+        self._args = (ctypes.byref(self.p), _ptr(sinks), _ptr(self.out), _out_code(out_dtype), _ptr(self.lse),
+                      _ptr(self.workspace), self.workspace.numel())
+
+    def run(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)))
+        return self.out, self.lse

@@ -144,7 +144,7 @@ int plan_segments(int num_reqs, int max_seq_len, int64_t sum_seq_lens, int num_h
   const mla::SegmentShape sh = mla::segment_shape(kv_dtype == MLA_DTYPE_FP8_E4M3, num_heads,
                                                   max_qlen < 1 ? 1 : max_qlen, tile);
   // Workgroups a CU holds at once (the LDS ring decides).
-  const int per_cu = mla::wgs_per_cu(sh.waves);
+  const int per_cu = mla::wgs_per_cu(sh.fp8, sh.waves);
   const int64_t slots = (int64_t)(num_cus > 0 ? num_cus : 256) * per_cu;
   const int64_t total = sum_seq_lens > 0 ? sum_seq_lens : (int64_t)num_reqs * max_seq_len;
   // Segments sized so the longest request's pieces match one slot's share of

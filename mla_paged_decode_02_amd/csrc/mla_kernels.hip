@@ -41,6 +41,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -152,9 +153,11 @@ __device__ __forceinline__ T lds_load(const char* base, int off) {
 }
 
 // NW waves x RG row groups of 16 rows per workgroup.
-// TT tokens per LDS tile (16 or 32; fp8 always uses 32).
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT>
-__global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
+// TT tokens per LDS tile (16 or 32; fp8 always uses 32).  OCC waves per SIMD
+// the register allocation must allow (2 caps a wave at 256 registers).
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void segment_kernel(
+    SegmentLaunch p) {
   using F = KvFmt<FP8>;
   static_assert(TT == 32 || (TT == 16 && !FP8), "tile shape");
   constexpr int kNB = TT / 16;                         // 16-token blocks per tile
@@ -225,18 +228,29 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
   const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
   const float sl2 = p.softmax_scale * kLog2e * qs * ks;
 
-  // ---- Q^T operand: lane (g, n) holds row n, dims 32c + 8g .. +7 ----
-  typedef typename std::conditional<FP8, long, bf16x8>::type QOp;
-  QOp qop[RG][18];
+  // ---- Q^T operand ----
+  // bf16: lane (g, n) holds row n, dims 32c + 8g .. +7 for c = 0..17.
+  // fp8:  latent dims 128c + 32g .. +31 for c = 0..3 (16x16x128 MFMA) and
+  //       rope dims 512 + 32c + 8g .. +7 for c = 0..1 (16x16x32 MFMA).
+  bf16x8 qop[FP8 ? 1 : RG][FP8 ? 1 : 18];
+  i32x8 qlat[FP8 ? RG : 1][4];
+  long qrope[FP8 ? RG : 1][2];
 #pragma unroll
   for (int q = 0; q < RG; ++q) {
     const int64_t qoff = (int64_t)(t0 + ti[q]) * p.q_stride_token + (int64_t)hh[q] * p.q_stride_head;
+    if constexpr (FP8) {
+      const uint8_t* qb = (const uint8_t*)p.q + qoff;
 #pragma unroll
-    for (int c = 0; c < 18; ++c) {
-      if constexpr (FP8) {
-        const uint8_t* qp = (const uint8_t*)p.q + qoff + 32 * c + 8 * g;
-        qop[q][c] = rok[q] ? *(const long*)qp : 0;
-      } else {
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 lo = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g) : u32x4{0, 0, 0, 0};
+        const u32x4 hi = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g + 16) : u32x4{0, 0, 0, 0};
+        qlat[q][c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) qrope[q][c] = rok[q] ? *(const long*)(qb + 512 + 32 * c + 8 * g) : 0;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 18; ++c) {
         const __bf16* qp = (const __bf16*)p.q + qoff + 32 * c + 8 * g;
         const u32x4 v = rok[q] ? *(const u32x4*)qp : u32x4{0, 0, 0, 0};
         qop[q][c] = __builtin_bit_cast(bf16x8, v);
@@ -367,10 +381,9 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
     kv_base[b] = lrow * F::kVPitch;
     kr_base[b] = kVRegion + lrow * F::kRopePitch;
     if constexpr (FP8) {
-      // logical chunk 2c + g/2, 8-byte half g & 1
-      kv_x[b] = (g >> 1) ^ swz_v(lrow);
+      // latent: logical chunks 8c + 2g (+1); rope: chunk 2c + g/2, half g & 1
+      kv_x[b] = (2 * g) ^ swz_v(lrow);
       kr_x[b] = (g >> 1) ^ F::swz_r(lrow);
-      kv_base[b] += 8 * (g & 1);
       kr_base[b] += 8 * (g & 1);
     } else {
       // logical chunk 4c + g
@@ -404,9 +417,17 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
     if (k < ntiles) issue_tile(k, k);
 
   for (int k = 0; k < ntiles; ++k) {
-    wait_tiles<kNIw, NBUF - 2>(min(NBUF - 2, ntiles - 1 - k));
-    __syncthreads();
-    if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+    if constexpr (NBUF == 1) {
+      // Single slot: load, wait, compute; other waves on the SIMD overlap.
+      if (k > 0) __syncthreads();  // every wave is done with the slot
+      issue_tile(k, 0);
+      wait_vmcnt<0>();
+      __syncthreads();
+    } else {
+      wait_tiles<kNIw, (NBUF >= 2 ? NBUF - 2 : 0)>(min(NBUF - 2, ntiles - 1 - k));
+      __syncthreads();
+      if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+    }
     if (!wave_has_rows) continue;
 
     const char* buf = lds[k % NBUF];
@@ -419,39 +440,71 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
       vtb[b] = opaque(vt_base[b]); vtx[b] = opaque(vt_x[b]);
     }
 
-    // S^T = K . Q^T for the tile's 16-token blocks: 18 * kNB (chunk, block)
-    // steps, operands prefetched kPF steps ahead.
-    typedef typename std::conditional<FP8, long, bf16x8>::type KOp;
-    constexpr int kPF = 4;
-    constexpr int kSteps = 18 * kNB;
-    auto k_off = [&](int st) {
-      const int c = st / kNB, b = st % kNB;
-      if (c < 16) {
-        const int lc = FP8 ? (2 * c) : (4 * c);  // logical chunk without the lane part
-        return kvb[b] + 16 * (lc ^ kvx[b]);
-      }
-      const int lc = FP8 ? (2 * (c - 16)) : (4 * (c - 16));
-      return krb[b] + 16 * (lc ^ krx[b]);
-    };
+    // S^T = K . Q^T for the tile's 16-token blocks.  LDS operands are
+    // prefetched several MFMA steps ahead: one MFMA issues every 16-32
+    // cycles, while an LDS read takes ~100-200 cycles to return.
+    // (8-wave workgroups run two waves per SIMD, which hide part of the
+    // latency for each other, and have half the registers: shallower there.)
+    constexpr int kPF = OCC == 2 ? 4 : 8;
     f32x4 sblk[RG][2];
 #pragma unroll
     for (int q = 0; q < RG; ++q) sblk[q][0] = sblk[q][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    KOp kop[kPF];
+    if constexpr (FP8) {
+      // latent: 4 x (16x16x128 f8f6f4) per block; steps (c, b), c = 0..3
+      auto lat_load = [&](int st) -> i32x8 {
+        const int c = st / kNB, b = st % kNB;
+        const u32x4 lo = lds_load<u32x4>(buf, kvb[b] + 16 * ((8 * c) ^ kvx[b]));
+        const u32x4 hi = lds_load<u32x4>(buf, kvb[b] + 16 * ((8 * c) ^ (kvx[b] ^ 1)));
+        return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int kLat = 4 * kNB;
+      constexpr int kPFL = OCC == 2 ? 2 : 4;
+      i32x8 kl[kPFL];
 #pragma unroll
-    for (int i = 0; i < kPF; ++i) kop[i] = lds_load<KOp>(buf, k_off(i));
+      for (int i = 0; i < kPFL; ++i) kl[i] = lat_load(i);
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      const KOp cur = kop[st % kPF];
-      if (st + kPF < kSteps) kop[st % kPF] = lds_load<KOp>(buf, k_off(st + kPF));
-      const int c = st / kNB, b = st % kNB;
+      for (int st = 0; st < kLat; ++st) {
+        const i32x8 cur = kl[st % kPFL];
+        if (st + kPFL < kLat) kl[st % kPFL] = lat_load(st + kPFL);
+        const int c = st / kNB, b = st % kNB;
 #pragma unroll
-      for (int q = 0; q < RG; ++q) {
-        if constexpr (FP8)
-          sblk[q][b] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(cur, qop[q][c], sblk[q][b], 0, 0, 0);
-        else
-          sblk[q][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qop[q][c], sblk[q][b], 0, 0, 0);
+        for (int q = 0; q < RG; ++q)
+          sblk[q][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur, qlat[q][c], sblk[q][b], 0, 0,
+                                                                         0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      // rope: 2 x (16x16x32 fp8) per block
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+          const long a = lds_load<long>(buf, krb[b] + 16 * ((2 * c) ^ krx[b]));
+#pragma unroll
+          for (int q = 0; q < RG; ++q)
+            sblk[q][b] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, qrope[q][c], sblk[q][b], 0, 0, 0);
+        }
+      }
+    } else {
+      // 18 * kNB (chunk, block) steps of 16x16x32 bf16
+      constexpr int kSteps = 18 * kNB;
+      auto k_off = [&](int st) {
+        const int c = st / kNB, b = st % kNB;
+        if (c < 16) return kvb[b] + 16 * ((4 * c) ^ kvx[b]);
+        return krb[b] + 16 * ((4 * (c - 16)) ^ krx[b]);
+      };
+      bf16x8 kop[kPF];
+#pragma unroll
+      for (int i = 0; i < kPF; ++i) kop[i] = lds_load<bf16x8>(buf, k_off(i));
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const bf16x8 cur = kop[st % kPF];
+        if (st + kPF < kSteps) kop[st % kPF] = lds_load<bf16x8>(buf, k_off(st + kPF));
+        const int c = st / kNB, b = st % kNB;
+#pragma unroll
+        for (int q = 0; q < RG; ++q)
+          sblk[q][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qop[q][c], sblk[q][b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // Base-2 online softmax per row over this tile.  The reference max m_run
@@ -459,6 +512,7 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
     // m_true tracks the exact max and the end rescales to it once.
     typedef typename std::conditional<kNB == 2, bf16x8, i16x4>::type POp;
     POp pb[RG];
+    long pb8[FP8 ? RG : 1];
     bool rescale = false;
     float alpha[RG];
 #pragma unroll
@@ -493,7 +547,14 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
       }
       m_run[q] = m_new;
       rescale |= alpha[q] != 1.f;
-      if constexpr (kNB == 2) {
+      if constexpr (FP8) {
+        // P^T in e4m3 for the fp8 P.V product (p <= 2^kLazy = 256 < 448)
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4], pv[5], 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[6], pv[7], w1, true);
+        pb8[q] = (long)(unsigned)w0 | ((long)(unsigned)w1 << 32);
+      } else if constexpr (kNB == 2) {
         pb[q] = to_bf16x8(pv);
       } else {
 #pragma unroll
@@ -501,14 +562,19 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
       }
     }
     if (__ballot(rescale)) {
+      // one accumulator group at a time: keeps the AGPR -> VGPR -> AGPR
+      // round trip to four registers
 #pragma unroll
       for (int q = 0; q < RG; ++q)
 #pragma unroll
-        for (int d = 0; d < 32; ++d) acc[q][d] *= alpha[q];
+        for (int d = 0; d < 32; ++d) {
+          acc[q][d] *= alpha[q];
+          __builtin_amdgcn_sched_barrier(0);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // O^T += V^T . P^T over 32 dim blocks of 16, operands prefetched kPF ahead.
+    // O^T += V^T . P^T over 32 dim blocks of 16, operands prefetched kPFV ahead.
     typedef typename std::conditional<FP8, i32x2, typename std::conditional<kNB == 2, bf16x8, i16x4>::type>::type VRaw;
     auto v_load = [&](int db) -> VRaw {
       if constexpr (kNB == 1) {
@@ -528,24 +594,27 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
-    VRaw vop[kPF];
+    constexpr int kPFV = OCC == 2 ? 4 : 8;
+    VRaw vop[kPFV];
 #pragma unroll
-    for (int i = 0; i < kPF; ++i) vop[i] = v_load(i);
+    for (int i = 0; i < kPFV; ++i) vop[i] = v_load(i);
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
-      const VRaw cur = vop[db % kPF];
-      if (db + kPF < 32) vop[db % kPF] = v_load(db + kPF);
+      const VRaw cur = vop[db % kPFV];
+      if (db + kPFV < 32) vop[db % kPFV] = v_load(db + kPFV);
       if constexpr (kNB == 1) {
 #pragma unroll
         for (int q = 0; q < RG; ++q)
           acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur, pb[q], acc[q][db], 0, 0, 0);
-      } else {
-        bf16x8 va;
-        if constexpr (FP8) va = fp8x8_to_bf16x8(__builtin_bit_cast(u32x2, cur));
-        else va = cur;
+      } else if constexpr (FP8) {
+        const long va = __builtin_bit_cast(long, cur);
 #pragma unroll
         for (int q = 0; q < RG; ++q)
-          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[q], acc[q][db], 0, 0, 0);
+          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va, pb8[q], acc[q][db], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < RG; ++q)
+          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pb[q], acc[q][db], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -557,7 +626,10 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
     const float f = (m_true[q] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[q] - m_true[q]);
     l_run[q] *= f;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) acc[q][d] *= f;
+    for (int d = 0; d < 32; ++d) {
+      acc[q][d] *= f;
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---- write this segment's partials ----
@@ -570,7 +642,10 @@ __global__ __launch_bounds__(64 * NW) void segment_kernel(SegmentLaunch p) {
     const int64_t slot = ((int64_t)(t0 + ti[q]) * H + hh[q]) * p.num_segments + s;
     float* outp = p.seg_out + slot * kKvRank + 4 * g;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) *(f32x4*)(outp + 16 * db) = acc[q][db] * ks;
+    for (int db = 0; db < 32; ++db) {
+      *(f32x4*)(outp + 16 * db) = acc[q][db] * ks;
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (g == 0) {
       p.seg_max[slot] = bad ? __builtin_nanf("") : m_true[q];
       p.seg_sum[slot] = l_tot;
@@ -730,21 +805,23 @@ hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
   // LDS ring per workgroup: 36 KiB with 1 wave (four workgroups per CU; bf16
   // uses 16-token tiles there), 72 KiB with 2 waves (two per CU), 144 KiB
   // with 4 waves (one per CU).
-  constexpr int kTT = tile_tokens(FP8, NW);
+  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW);
+  constexpr int kTT = kCfg.tt;
   constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
-  constexpr int kRing = ring_bytes(NW) / kTileBytes;
+  constexpr int kRing = kCfg.ring / kTileBytes;
   dim3 grid(a.num_segments, a.num_reqs, chunks);
-  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG, kTT>), grid, dim3(64 * NW), 0, stream, a);
+  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ>), grid, dim3(64 * NW), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 template <bool FP8, bool CONTIG>
 hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, hipStream_t stream) {
-  if (sh.rows_per_wave == 2) return launch_seg<FP8, 4, 2, CONTIG>(a, sh.chunks, stream);
   switch (sh.waves) {
     case 1: return launch_seg<FP8, 1, 1, CONTIG>(a, sh.chunks, stream);
     case 2: return launch_seg<FP8, 2, 1, CONTIG>(a, sh.chunks, stream);
-    default: return launch_seg<FP8, 4, 1, CONTIG>(a, sh.chunks, stream);
+    case 4: return launch_seg<FP8, 4, 1, CONTIG>(a, sh.chunks, stream);
+    default: return launch_seg<FP8, 8, 1, CONTIG>(a, sh.chunks, stream);
   }
 }
 
@@ -758,7 +835,7 @@ SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
   if (groups <= 1)      { sh.waves = 1; sh.rows_per_wave = 1; }
   else if (groups == 2) { sh.waves = 2; sh.rows_per_wave = 1; }
   else if (groups <= 4) { sh.waves = 4; sh.rows_per_wave = 1; }
-  else                  { sh.waves = 4; sh.rows_per_wave = 2; }
+  else                  { sh.waves = 8; sh.rows_per_wave = 1; }
   const int per_wg = sh.waves * sh.rows_per_wave;
   sh.chunks = (groups + per_wg - 1) / per_wg;
   sh.contig = tile >= tile_tokens(fp8, sh.waves);

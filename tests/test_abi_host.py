@@ -58,7 +58,7 @@ def test_segment_bounds_match_oracle(S, tile):
 def test_planner_fills_the_chip():
     # uniform bs=52 x 16K: workgroups x per-CU capacity
     assert m.plan_num_segments(52, 16384, 16, tile_size=64) == 19    # 1 wave/WG, 4 WGs/CU
-    assert m.plan_num_segments(52, 16384, 64, tile_size=64) == 4     # 4 waves/WG, 1 WG/CU
+    assert m.plan_num_segments(52, 16384, 64, tile_size=64) == 9     # 4 waves/WG, 2 WGs/CU
     assert m.plan_num_segments(52, 16384, 128, tile_size=128) == 4
     assert m.plan_num_segments(1, 100, 16, tile_size=16) == 7        # capped at cdiv(100, 16)
     assert m.plan_num_segments(4000, 1000, 16, tile_size=64) == 1

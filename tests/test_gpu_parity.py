@@ -222,3 +222,18 @@ def test_poison_never_read():
                          dtype="bf16", seed=71, extra_bt_cols=3)
     out, lse = run_decode(w, num_segments=2)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_prepared_decoder_matches_decode():
+    """The prepared call gives the bits of the one-shot call, run after run."""
+    import mla_paged_decode_02_amd as m
+    w = mi.make_workload(name="prep", seq_lens=[1500, 64, 333], num_heads=16, block_size=64,
+                         dtype="bf16", sinks=True, seed=81)
+    d = mi.to_torch(w, "cuda")
+    args = mi.call_args(w, d)
+    o1, l1 = m.decode(**args, sinks=d["sinks"], num_segments=3)
+    dec = m.Decoder(**args, sinks=d["sinks"], num_segments=3)
+    for _ in range(3):
+        o2, l2 = dec.run()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
