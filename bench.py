@@ -154,11 +154,39 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     alg = kv_bytes + q_bytes + part_bytes
     achieved = alg / (seg_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(name),
             "kernel": "segment_kernel", "kernel_us": round(seg_ms * 1e3, 2),
             "algorithmic_bytes": alg}
     res["segment_kernel_us"] = seg_ms * 1e3
     return w, res, roof
+
+
+KERNEL_SOURCES = ("mla_paged_decode_02_amd/csrc/mla_kernels.hip", "mla_paged_decode_02_amd/csrc/mla_internal.h")
+
+
+def profiled_traffic(workload):
+    """HBM bytes per segment-kernel launch from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary of this workload (copy-calibrated), or
+    None when there is none or the kernel sources changed since it was taken."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        kv = {}
+        with open(path) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith(("|", "#", " ")):
+                    k, _, v = line.partition(":")
+                    kv[k.strip()] = v.strip()
+        if (kv.get("workload") == workload and kv.get("kernel_source_sha256_16") == digest
+                and "segment_kernel_traffic_bytes" in kv):
+            return int(kv["segment_kernel_traffic_bytes"])
+    return None
 
 
 def cpu_baseline(w, nreq):
