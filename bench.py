@@ -31,12 +31,13 @@ METRIC = "µs per MLA decode step and effective KV HBM GB/s (bs=52, 16K ctx, H=1
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {
-    # name: (num_heads, dtype, block, seed)
-    "bs52_ctx16k_h16_bf16_blk64": (16, "bf16", 64, 2),
-    "bs52_ctx16k_h16_fp8_blk64": (16, "fp8_e4m3", 64, 3),
-    "bs52_ctx16k_h48_fp8_blk64": (48, "fp8_e4m3", 64, 3),
-    "bs52_ctx16k_h64_fp8_blk64": (64, "fp8_e4m3", 64, 3),
-    "bs52_ctx16k_h128_bf16_blk256": (128, "bf16", 256, 4),
+    # name: workload constructor (seeded; see mla_inputs)
+    "bs52_ctx16k_h16_bf16_blk64": lambda mi: mi.bs52_h16_bf16(),
+    "bs52_ctx16k_h16_fp8_blk64": lambda mi: mi.bs52_fp8(16),
+    "bs52_ctx16k_h48_fp8_blk64": lambda mi: mi.bs52_fp8(48),
+    "bs52_ctx16k_h64_fp8_blk64": lambda mi: mi.bs52_fp8(64),
+    "bs52_ctx16k_h128_bf16_blk256": lambda mi: mi.bs52_h128_bf16(),
+    "ragged128_max32k_h96_fp8_causal_sinks": lambda mi: mi.ragged_h96_fp8(),
 }
 DEFAULT = "bs52_ctx16k_h16_bf16_blk64"
 
@@ -70,14 +71,31 @@ def copy_calibration(torch, reps=5):
 
 
 def build_inputs(name, torch, mi):
-    H, dtype, block, seed = WORKLOADS[name]
-    w = mi.uniform_batch(num_heads=H, dtype=dtype, block_size=block, bs=52, ctx=16384, seed=seed,
-                         name=name)
+    w = WORKLOADS[name](mi)
+    w.name = name
     d = mi.to_torch(w, "cuda")
     # a second cache copy (same contents, other addresses) for alternating steps
     d2 = dict(d)
     d2["kv_cache"] = d["kv_cache"].clone()
     return w, [d, d2]
+
+
+WARMUP_FLOOR_S = 0.3
+
+
+def warmup(fn, n, torch):
+    """n untimed calls, continued until WARMUP_FLOOR_S has passed: the GPU
+    clocks take some tens of milliseconds to settle after the first launches,
+    and a handful of 0.2 ms steps would otherwise be timed during that ramp."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < n or time.perf_counter() - t0 < WARMUP_FLOOR_S:
+        fn(i)
+        i += 1
+        if i % 32 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
 
 def time_workload(name, args, torch, m, mi, want_roofline):
@@ -86,16 +104,15 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     kv_bytes = w.kv_bytes_touched()
     calls = [mi.call_args(w, d) for d in ds]
     # One prepared call per cache copy: each step is a single C call.
-    decs = [m.Decoder(**c, num_segments=args.num_segments, out_dtype=torch.bfloat16) for c in calls]
+    decs = [m.Decoder(**c, sinks=d["sinks"], num_segments=args.num_segments, out_dtype=torch.bfloat16)
+            for c, d in zip(calls, ds)]
     S = decs[0].num_segments
     stream = torch.cuda.current_stream()
 
     def step(i):
         decs[i & 1].run(stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_s = warmup(step, args.warmup, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
@@ -105,7 +122,10 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     ms = e0.elapsed_time(e1) / args.steps
 
     res = {"workload": name, "num_heads": w.num_heads, "dtype": w.kv_dtype, "num_segments": S,
-           "us_per_step": ms * 1e3, "kv_bytes": kv_bytes,
+           "num_reqs": w.num_reqs, "num_tokens": w.num_tokens, "max_qlen": w.max_qlen,
+           "max_seq_len": w.max_seq_len, "block_size": w.block_size, "causal": bool(w.causal),
+           "sinks": w.sinks is not None,
+           "us_per_step": ms * 1e3, "kv_bytes": kv_bytes, "warmup_s": round(warm_s, 3),
            "eff_kv_GBps": kv_bytes / (ms * 1e-3) / 1e9,
            "frac_of_hbm_peak": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if not want_roofline:
@@ -117,10 +137,8 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     so = torch.empty((T, H, S, 512), dtype=torch.float32, device="cuda")
     sm = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
     se = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
-    for i in range(args.warmup):
-        m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
-                          segm_expsum=se, stream=stream)
-    torch.cuda.synchronize()
+    warmup(lambda i: m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
+                                       segm_expsum=se, stream=stream), args.warmup, torch)
     e0.record(stream)
     for i in range(args.steps):
         m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
@@ -129,16 +147,16 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     torch.cuda.synchronize()
     seg_ms = e0.elapsed_time(e1) / args.steps
     # Merge kernel alone on the same partials.
-    part_lens = ds[0]["seq_lens"]
+    qlens = torch.diff(ds[0]["qo_indptr"])
+    part_lens = torch.repeat_interleave(ds[0]["seq_lens"], qlens).to(torch.int32)
     mo = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
     ml = torch.empty((T, H), dtype=torch.float32, device="cuda")
     tile = w.tile_size or m.tile_size_for_block(w.block_size)
-    for i in range(args.warmup):
-        m.merge_segments(so, sm, se, part_lens, tile, out=mo, lse=ml, stream=stream)
-    torch.cuda.synchronize()
+    warmup(lambda i: m.merge_segments(so, sm, se, part_lens, tile, sinks=ds[0]["sinks"], out=mo, lse=ml,
+                                      stream=stream), args.warmup, torch)
     e0.record(stream)
     for i in range(args.steps):
-        m.merge_segments(so, sm, se, part_lens, tile, out=mo, lse=ml, stream=stream)
+        m.merge_segments(so, sm, se, part_lens, tile, sinks=ds[0]["sinks"], out=mo, lse=ml, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
     merge_ms = e0.elapsed_time(e1) / args.steps
@@ -147,8 +165,9 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     # Algorithmic bytes of one segment-kernel launch: every cache row once,
     # q once, the fp32 partials of every valid segment written once.
     import mla_paged_decode_02_amd as mm
-    valid = sum(len(mm.segment_bounds(int(L), S, w.tile_size or mm.tile_size_for_block(w.block_size)))
-                for L in w.seq_lens)
+    qlen_r = [int(x) for x in (w.qo_indptr[1:] - w.qo_indptr[:-1])]
+    valid = sum(ql * len(mm.segment_bounds(int(L), S, w.tile_size or mm.tile_size_for_block(w.block_size)))
+                for L, ql in zip(w.seq_lens, qlen_r))
     q_bytes = T * H * 576 * esz
     part_bytes = valid * H * (512 + 2) * 4
     alg = kv_bytes + q_bytes + part_bytes
@@ -245,6 +264,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_s": res["warmup_s"],
         "ms_per_step": round(res["us_per_step"] / 1e3, 5),
         "us_per_step": round(res["us_per_step"], 2),
         "higher_is_better": True,
@@ -252,8 +272,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8_e4m3",
         "data": "synthetic (seeded N(0,1) q and latent cache, random page permutation)",
-        "config": {"workload": res["workload"], "batch": 52, "qlen": 1, "kv_tokens_per_request": 16384,
-                   "num_heads": res["num_heads"], "block_size": WORKLOADS[res["workload"]][2],
+        "config": {"workload": res["workload"], "batch": res["num_reqs"], "tokens": res["num_tokens"],
+                   "max_qlen": res["max_qlen"], "max_kv_tokens_per_request": res["max_seq_len"],
+                   "num_heads": res["num_heads"], "block_size": res["block_size"],
+                   "causal": res["causal"], "sinks": res["sinks"],
                    "num_segments": res["num_segments"], "parallelism": "single GPU"},
         "frac_of_hbm_peak": round(res["frac_of_hbm_peak"], 4),
         "roofline": roof,

@@ -303,4 +303,5 @@ def call_args(w: Workload, d: dict, *, use_indptr: Optional[bool] = None) -> dic
                 seq_lens=d["seq_lens"], softmax_scale=w.softmax_scale,
                 max_seq_len=w.max_seq_len, qo_indptr=d["qo_indptr"] if use_indptr else None,
                 max_qlen=w.max_qlen if use_indptr else None, causal=w.causal,
-                q_scale=d["q_scale"], kv_scale=d["kv_scale"], tile_size=w.tile_size)
+                q_scale=d["q_scale"], kv_scale=d["kv_scale"], tile_size=w.tile_size,
+                sum_seq_lens=int(np.asarray(w.seq_lens, dtype=np.int64).sum()))

@@ -260,13 +260,14 @@ def workspace_bytes(p: MlaProblem) -> int:
 
 def decode_segments(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, num_segments: int,
                     max_seq_len: int, qo_indptr=None, max_qlen=None, causal=False, q_scale=None,
-                    kv_scale=None, tile_size: int = 0, segm_output=None, segm_max=None,
-                    segm_expsum=None, stream=None):
+                    kv_scale=None, tile_size: int = 0, sum_seq_lens: int = 0, segm_output=None,
+                    segm_max=None, segm_expsum=None, stream=None):
     """Base-2 partials [T, H, S, 512], [T, H, S], [T, H, S] (fp32).  Slots of
     segments that hold no position are left as allocated (uninitialised)."""
     p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                      max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen, causal=causal,
-                     q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size, num_segments=num_segments)
+                     q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size, num_segments=num_segments,
+                     sum_seq_lens=sum_seq_lens)
     T, H, S = q.shape[0], q.shape[1], int(num_segments)
     dev = q.device
     if segm_output is None:
