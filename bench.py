@@ -122,6 +122,7 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     ms = e0.elapsed_time(e1) / args.steps
 
     res = {"workload": name, "num_heads": w.num_heads, "dtype": w.kv_dtype, "num_segments": S,
+           "split_workgroups": decs[0].split_workgroups,
            "num_reqs": w.num_reqs, "num_tokens": w.num_tokens, "max_qlen": w.max_qlen,
            "max_seq_len": w.max_seq_len, "block_size": w.block_size, "causal": bool(w.causal),
            "sinks": w.sinks is not None,
@@ -131,53 +132,97 @@ def time_workload(name, args, torch, m, mi, want_roofline):
     if not want_roofline:
         return w, res, None
 
-    # Segment kernel alone (the dominant kernel), timed with events on the
-    # stream it is launched on.
     T, H = w.num_tokens, w.num_heads
-    so = torch.empty((T, H, S, 512), dtype=torch.float32, device="cuda")
-    sm = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
-    se = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
-    warmup(lambda i: m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
-                                       segm_expsum=se, stream=stream), args.warmup, torch)
-    e0.record(stream)
-    for i in range(args.steps):
-        m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
-                          segm_expsum=se, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    seg_ms = e0.elapsed_time(e1) / args.steps
-    # Merge kernel alone on the same partials.
-    qlens = torch.diff(ds[0]["qo_indptr"])
-    part_lens = torch.repeat_interleave(ds[0]["seq_lens"], qlens).to(torch.int32)
-    mo = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
-    ml = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    tile = w.tile_size or m.tile_size_for_block(w.block_size)
-    warmup(lambda i: m.merge_segments(so, sm, se, part_lens, tile, sinks=ds[0]["sinks"], out=mo, lse=ml,
-                                      stream=stream), args.warmup, torch)
-    e0.record(stream)
-    for i in range(args.steps):
-        m.merge_segments(so, sm, se, part_lens, tile, sinks=ds[0]["sinks"], out=mo, lse=ml, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    merge_ms = e0.elapsed_time(e1) / args.steps
-    res["merge_kernel_us"] = merge_ms * 1e3
-
-    # Algorithmic bytes of one segment-kernel launch: every cache row once,
-    # q once, the fp32 partials of every valid segment written once.
-    import mla_paged_decode_02_amd as mm
-    qlen_r = [int(x) for x in (w.qo_indptr[1:] - w.qo_indptr[:-1])]
-    valid = sum(ql * len(mm.segment_bounds(int(L), S, w.tile_size or mm.tile_size_for_block(w.block_size)))
-                for L, ql in zip(w.seq_lens, qlen_r))
+    out_esz = 2  # bf16 output
     q_bytes = T * H * 576 * esz
-    part_bytes = valid * H * (512 + 2) * 4
-    alg = kv_bytes + q_bytes + part_bytes
-    achieved = alg / (seg_ms * 1e-3) / 1e9
+    if decs[0].split is not None:
+        # Balanced split: stage 1 (the cache stream, the dominant kernel) and
+        # stage 2 (the merge of requests cut by a range boundary), each timed
+        # alone with events on the stream it is launched on.
+        stage_us = {}
+        for stage in (1, 2):
+            warmup(lambda i: decs[i & 1].run_stage(stage, stream), args.warmup, torch)
+            e0.record(stream)
+            for i in range(args.steps):
+                decs[i & 1].run_stage(stage, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            stage_us[stage] = e0.elapsed_time(e1) / args.steps * 1e3
+        sched = split_schedule(w, *decs[0].split)
+        alg = kv_bytes + q_bytes + sched["final_rows"] * (512 * out_esz + 4) + sched["partial_rows"] * (512 + 2) * 4
+        kernel, kernel_us = "split_kernel", stage_us[1]
+        res["split"] = {"workgroups": decs[0].split[0], "rows_per_workgroup": decs[0].split[1],
+                        "unit_keys": decs[0].split[2], **sched}
+        res["merge_kernel_us"] = stage_us[2]
+    else:
+        # Segment partition: segment kernel and merge kernel each timed alone.
+        S = decs[0].num_segments
+        so = torch.empty((T, H, S, 512), dtype=torch.float32, device="cuda")
+        sm = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
+        se = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
+        warmup(lambda i: m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
+                                           segm_expsum=se, stream=stream), args.warmup, torch)
+        e0.record(stream)
+        for i in range(args.steps):
+            m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
+                              segm_expsum=se, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        seg_ms = e0.elapsed_time(e1) / args.steps
+        qlens = torch.diff(ds[0]["qo_indptr"])
+        part_lens = torch.repeat_interleave(ds[0]["seq_lens"], qlens).to(torch.int32)
+        mo = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+        ml = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        tile = w.tile_size or m.tile_size_for_block(w.block_size)
+        warmup(lambda i: m.merge_segments(so, sm, se, part_lens, tile, sinks=ds[0]["sinks"], out=mo, lse=ml,
+                                          stream=stream), args.warmup, torch)
+        e0.record(stream)
+        for i in range(args.steps):
+            m.merge_segments(so, sm, se, part_lens, tile, sinks=ds[0]["sinks"], out=mo, lse=ml, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["merge_kernel_us"] = e0.elapsed_time(e1) / args.steps * 1e3
+        qlen_r = [int(x) for x in (w.qo_indptr[1:] - w.qo_indptr[:-1])]
+        valid = sum(ql * len(m.segment_bounds(int(L), S, tile)) for L, ql in zip(w.seq_lens, qlen_r))
+        alg = kv_bytes + q_bytes + valid * H * (512 + 2) * 4
+        kernel, kernel_us = "segment_kernel", seg_ms * 1e3
+    achieved = alg / (kernel_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(name),
-            "kernel": "segment_kernel", "kernel_us": round(seg_ms * 1e3, 2),
-            "algorithmic_bytes": alg}
-    res["segment_kernel_us"] = seg_ms * 1e3
+            "kernel": kernel, "kernel_us": round(kernel_us, 2), "algorithmic_bytes": int(alg)}
+    res["segment_kernel_us"] = kernel_us
     return w, res, roof
+
+
+def split_schedule(w, G, rows_wg, tt):
+    """Rows the balanced split finishes in place and partial rows it writes,
+    from the same unit layout the split kernel uses (request, row chunk, tile;
+    workgroup g takes units [g W / G, (g+1) W / G))."""
+    H = w.num_heads
+    qo = [int(x) for x in w.qo_indptr]
+    jobs = []  # (first unit, units, rows)
+    off = 0
+    for r, L in enumerate(int(x) for x in w.seq_lens):
+        rows = (qo[r + 1] - qo[r]) * H
+        nt = -(-L // tt) if L > 0 else 0
+        nch = -(-rows // rows_wg) if nt else 0
+        for c in range(nch):
+            jobs.append((off + c * nt, nt, min(rows_wg, rows - c * rows_wg)))
+        off += nch * nt
+    W = off
+    final_rows = partial_rows = pieces = 0
+    for P, nt, rows in jobs:
+        gf = ((P + 1) * G - 1) // W
+        gl = ((P + nt) * G - 1) // W
+        if gf == gl:
+            final_rows += rows
+        else:
+            # workgroups with an empty range (G > W) hold no piece
+            n = sum(1 for g in range(gf, gl + 1) if ((g + 1) * W) // G > (g * W) // G)
+            pieces += n
+            partial_rows += n * rows
+    return {"units": W, "jobs": len(jobs), "final_rows": final_rows, "partial_rows": partial_rows,
+            "split_pieces": pieces}
 
 
 KERNEL_SOURCES = ("mla_paged_decode_02_amd/csrc/mla_kernels.hip", "mla_paged_decode_02_amd/csrc/mla_internal.h")
@@ -276,11 +321,13 @@ def main():
                    "max_qlen": res["max_qlen"], "max_kv_tokens_per_request": res["max_seq_len"],
                    "num_heads": res["num_heads"], "block_size": res["block_size"],
                    "causal": res["causal"], "sinks": res["sinks"],
-                   "num_segments": res["num_segments"], "parallelism": "single GPU"},
+                   "num_segments": res["num_segments"], "split_workgroups": res["split_workgroups"],
+                   "parallelism": "single GPU"},
         "frac_of_hbm_peak": round(res["frac_of_hbm_peak"], 4),
         "roofline": roof,
-        "segment_kernel_us": round(res.get("segment_kernel_us", 0.0), 2),
+        "stream_kernel_us": round(res.get("segment_kernel_us", 0.0), 2),
         "merge_kernel_us": round(res.get("merge_kernel_us", 0.0), 2),
+        "split": res.get("split"),
         "cpu_baseline": cpu,
         "extra": extra,
         "wall_s": round(time.time() - t0, 1),

@@ -115,7 +115,10 @@ typedef struct mla_problem {
   float softmax_scale; /* scores = softmax_scale * (q . row) over all 576 dims */
   int32_t tile_size;   /* 0 = min(128, largest power-of-two divisor of block_size);
                           else a power of two <= 128 dividing block_size */
-  int32_t num_segments; /* S >= 1 (mla_decode also accepts 0 = planner's choice) */
+  int32_t num_segments; /* S >= 1 (mla_decode also accepts 0 = balanced split) */
+  int32_t max_workgroups; /* balanced split: at most this many workgroups
+                             (0 = as many as the device holds at once), e.g.
+                             to leave compute units to concurrent work */
 } mla_problem;
 
 /*
@@ -160,20 +163,48 @@ int mla_merge_segments(const float* segm_output, const float* segm_max, const fl
                        void* stream);
 
 /*
- * Fused decode: segments + merge in two stream-ordered launches, the partials
- * living in the caller's workspace (>= mla_decode_workspace_bytes(p) bytes,
- * 256-byte aligned).  num_segments == 0 lets the planner choose S.
- * sinks / out / out_dtype / lse as for mla_merge_segments.
+ * Fused decode: out [T, H, 512] and lse [T, H] in two stream-ordered
+ * launches, partial results living in the caller's workspace
+ * (>= mla_decode_workspace_bytes(p) bytes, 256-byte aligned; its contents on
+ * entry do not matter).  sinks / out / out_dtype / lse as for
+ * mla_merge_segments.
+ *  - num_segments >= 1: the segment partition above with that S, then the
+ *    merge (the same results as mla_decode_segments + mla_merge_segments).
+ *  - num_segments == 0: a balanced split of the key axis.  The batch's work is
+ *    one sequence of units (request, row chunk, tile of TT keys) that is cut
+ *    into equal ranges, one per workgroup, so every compute unit streams the
+ *    same number of cache rows whatever the lengths.  A (request, row chunk)
+ *    inside one range is finished by the first launch; one cut by a range
+ *    boundary is merged by the second from per-piece base-2 partials (the
+ *    same merge rule as above).  The result equals the num_segments >= 1
+ *    result up to floating-point rounding.
  */
 int mla_decode(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace mla_decode needs for p (uses the planner when num_segments == 0).
- * Returns 0 and sets *bytes, or an error. */
+/*
+ * One of the two launches of mla_decode, for callers that schedule them
+ * separately (e.g. to place other work between them, or to time them):
+ * stage 1 streams the cache (and, with num_segments == 0, finishes the rows
+ * whose keys fell in one workgroup), stage 2 merges.  Stage 2 must follow
+ * stage 1 on the same workspace.  Arguments as for mla_decode.
+ */
+int mla_decode_stage(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
+                     void* workspace, size_t workspace_bytes, int32_t stage, void* stream);
+
+/* Workspace mla_decode needs for p.  Returns 0 and sets *bytes, or an error. */
 int mla_decode_workspace_bytes(const mla_problem* p, size_t* bytes);
 
-/* The S mla_decode would use for p (host only after the first call on a
- * device: reads the CU count once). Returns S >= 1 or an error. */
+/* The balanced split mla_decode uses for p (num_segments == 0): workgroups,
+ * query rows per workgroup and keys per unit (TT).  Returns 1 and fills the
+ * outputs (each may be NULL); 0 when p uses the segment partition instead;
+ * or an error. */
+int mla_split_plan(const mla_problem* p, int32_t* workgroups, int32_t* rows_per_workgroup,
+                   int32_t* unit_keys);
+
+/* The S the planner gives p when num_segments == 0 (for the segment entry
+ * points; host only after the first call on a device: reads the CU count
+ * once), else p->num_segments.  Returns S >= 1 or an error. */
 int mla_resolve_num_segments(const mla_problem* p);
 
 /* Planner (pure host): S so that request x segment work items fill num_cus

@@ -77,6 +77,7 @@ class MlaProblem(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("tile_size", ctypes.c_int32),
         ("num_segments", ctypes.c_int32),
+        ("max_workgroups", ctypes.c_int32),
     ]
 
 
@@ -86,7 +87,7 @@ EXPORTED = (
     "mla_validate", "mla_decode_segments", "mla_merge_segments", "mla_decode",
     "mla_decode_workspace_bytes", "mla_resolve_num_segments", "mla_plan_num_segments",
     "mla_tile_size_for_block", "mla_segment_bounds", "mla_status_string", "mla_last_error",
-    "mla_version",
+    "mla_version", "mla_decode_stage", "mla_split_plan",
 )
 
 
@@ -104,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_segments.argtypes = [P, vp, vp, vp, vp]
     L.mla_merge_segments.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp]
     L.mla_decode.argtypes = [P, vp, vp, i32, vp, vp, sz, vp]
+    L.mla_decode_stage.argtypes = [P, vp, vp, i32, vp, vp, sz, i32, vp]
+    L.mla_split_plan.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.mla_decode_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     L.mla_resolve_num_segments.argtypes = [P]
     L.mla_plan_num_segments.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32]
@@ -116,7 +119,8 @@ def lib() -> ctypes.CDLL:
     L.mla_version.argtypes = []
     for f in ("mla_validate", "mla_decode_segments", "mla_merge_segments", "mla_decode",
               "mla_decode_workspace_bytes", "mla_resolve_num_segments", "mla_plan_num_segments",
-              "mla_tile_size_for_block", "mla_segment_bounds", "mla_version"):
+              "mla_tile_size_for_block", "mla_segment_bounds", "mla_version", "mla_decode_stage",
+              "mla_split_plan"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -198,7 +202,7 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
                  qo_indptr: Optional[torch.Tensor] = None, max_qlen: Optional[int] = None,
                  causal: bool = False, q_scale: Optional[torch.Tensor] = None,
                  kv_scale: Optional[torch.Tensor] = None, tile_size: int = 0,
-                 num_segments: int = 0, sum_seq_lens: int = 0) -> MlaProblem:
+                 num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0) -> MlaProblem:
     """Fill an ``mla_problem`` from tensors.  Host ints (max_seq_len, max_qlen)
     are passed by the caller so nothing is read back from the device."""
     if q.ndim != 3 or q.shape[-1] != HEAD_DIM or q.stride(-1) != 1:
@@ -239,6 +243,7 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
     p.softmax_scale = float(softmax_scale)
     p.tile_size = int(tile_size)
     p.num_segments = int(num_segments)
+    p.max_workgroups = int(max_workgroups)
     return p
 
 
@@ -248,6 +253,14 @@ def validate(p: MlaProblem, require_segments: bool = True) -> None:
 
 def resolve_num_segments(p: MlaProblem) -> int:
     return _check(lib().mla_resolve_num_segments(ctypes.byref(p)))
+
+
+def split_plan(p: MlaProblem):
+    """(workgroups, rows per workgroup, keys per unit) of the balanced split
+    ``decode`` uses for p, or None when p uses the segment partition."""
+    g, rw, tt = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    used = _check(lib().mla_split_plan(ctypes.byref(p), ctypes.byref(g), ctypes.byref(rw), ctypes.byref(tt)))
+    return (g.value, rw.value, tt.value) if used else None
 
 
 def workspace_bytes(p: MlaProblem) -> int:
@@ -303,13 +316,13 @@ def merge_segments(segm_output, segm_max, segm_expsum, part_lens, tile_size: int
 
 def decode(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_len: int,
            qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
-           tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0,
+           tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0,
            out_dtype=torch.bfloat16, out=None, lse=None, workspace=None, stream=None):
     """Fused decode: returns (out [T, H, 512], lse [T, H])."""
     p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                      max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen, causal=causal,
                      q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
-                     num_segments=num_segments, sum_seq_lens=sum_seq_lens)
+                     num_segments=num_segments, sum_seq_lens=sum_seq_lens, max_workgroups=max_workgroups)
     T, H = q.shape[0], q.shape[1]
     check_sinks(sinks, H)
     if out is None:
@@ -337,13 +350,18 @@ class Decoder:
     def __init__(self, q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_len: int,
                  qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
                  tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0,
-                 out_dtype=torch.bfloat16):
+                 max_workgroups: int = 0, out_dtype=torch.bfloat16):
         self.p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                               max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen,
                               causal=causal, q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
-                              num_segments=num_segments, sum_seq_lens=sum_seq_lens)
+                              num_segments=num_segments, sum_seq_lens=sum_seq_lens,
+                              max_workgroups=max_workgroups)
         check_sinks(sinks, q.shape[1])
-        self.num_segments = resolve_num_segments(self.p)
+        # num_segments == 0 keeps the balanced split (split_workgroups > 0);
+        # otherwise the segment partition with that S.
+        self.split = split_plan(self.p)
+        self.split_workgroups = self.split[0] if self.split else 0
+        self.num_segments = 0 if self.split else resolve_num_segments(self.p)
         self.p.num_segments = self.num_segments
         T, H = q.shape[0], q.shape[1]
         self.out = torch.empty((T, H, KV_LORA_RANK), dtype=out_dtype, device=q.device)
@@ -356,4 +374,9 @@ class Decoder:
 
     def run(self, stream=None):
         _check(self._fn(*self._args, _stream(stream)))
+        return self.out, self.lse
+
+    def run_stage(self, stage: int, stream=None):
+        """One of the two launches of ``run`` (1: cache stream, 2: merge)."""
+        _check(lib().mla_decode_stage(*self._args, int(stage), _stream(stream)))
         return self.out, self.lse

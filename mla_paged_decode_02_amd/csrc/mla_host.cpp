@@ -97,6 +97,8 @@ int validate(const mla_problem* p, bool require_segments) {
                 p->num_segments);
   if (p->num_segments > MLA_MAX_SEGMENTS)
     return fail(MLA_ERR_INVALID_ARG, "num_segments %d > %d", p->num_segments, MLA_MAX_SEGMENTS);
+  if (p->max_workgroups < 0)
+    return fail(MLA_ERR_INVALID_ARG, "max_workgroups must be >= 0, got %d", p->max_workgroups);
   if (p->max_seq_len < 0) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be >= 0");
   if (p->qo_indptr == nullptr) {
     if (p->num_tokens != p->num_reqs)
@@ -144,7 +146,7 @@ int plan_segments(int num_reqs, int max_seq_len, int64_t sum_seq_lens, int num_h
   const mla::SegmentShape sh = mla::segment_shape(kv_dtype == MLA_DTYPE_FP8_E4M3, num_heads,
                                                   max_qlen < 1 ? 1 : max_qlen, tile);
   // Workgroups a CU holds at once (the LDS ring decides).
-  const int per_cu = mla::wgs_per_cu(sh.fp8, sh.waves);
+  const int per_cu = mla::wgs_per_cu(sh.fp8, sh.waves, sh.rows_per_wave);
   const int64_t slots = (int64_t)(num_cus > 0 ? num_cus : 256) * per_cu;
   const int64_t total = sum_seq_lens > 0 ? sum_seq_lens : (int64_t)num_reqs * max_seq_len;
   // Segments sized so the longest request's pieces match one slot's share of
@@ -157,11 +159,54 @@ int plan_segments(int num_reqs, int max_seq_len, int64_t sum_seq_lens, int num_h
   return (int)S;
 }
 
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Balanced split of the fused decode (num_segments == 0): the split kernel's
+// shape and workgroup count.  grid_wgs == 0 means "use the segment formula"
+// (the unit count would not fit 32 bits).
+struct SplitPlan {
+  mla::SegmentShape sh;
+  int rows_wg, tt, grid_wgs;
+};
+
+SplitPlan plan_split(const mla_problem* p, int tile) {
+  SplitPlan sp;
+  const int max_qlen = p->qo_indptr ? p->max_qlen : 1;
+  sp.sh = mla::segment_shape(p->kv_dtype == MLA_DTYPE_FP8_E4M3, p->num_heads, max_qlen, tile);
+  sp.rows_wg = 16 * sp.sh.waves * sp.sh.rows_per_wave;
+  sp.tt = mla::tile_tokens(sp.sh.fp8, sp.sh.waves, sp.sh.rows_per_wave);
+  const int64_t chunks = cdiv64((int64_t)max_qlen * p->num_heads, sp.rows_wg);
+  const int64_t max_units = (int64_t)p->num_reqs * chunks * cdiv64(p->max_seq_len > 0 ? p->max_seq_len : 1, sp.tt);
+  if (max_units >= ((int64_t)1 << 31)) { sp.grid_wgs = 0; return sp; }
+  // Units the batch holds at most (exact up to one tile per request when the
+  // caller gives the summed lengths).
+  const int64_t est = p->sum_seq_lens > 0 ? chunks * (cdiv64(p->sum_seq_lens, sp.tt) + p->num_reqs) : max_units;
+  const int64_t slots = (int64_t)device_cus() * mla::wgs_per_cu(sp.sh.fp8, sp.sh.waves, sp.sh.rows_per_wave);
+  int64_t G = slots < est ? slots : est;
+  if (p->max_workgroups > 0 && G > p->max_workgroups) G = p->max_workgroups;
+  if (G < 1) G = 1;
+  sp.grid_wgs = (int)G;
+  return sp;
+}
+
+struct SplitWs {
+  size_t out_off, max_off, sum_off, off_off, total;
+};
+
+SplitWs split_ws(const SplitPlan& sp, int num_reqs) {
+  SplitWs w;
+  const size_t rows = (size_t)sp.grid_wgs * 2 * sp.rows_wg;
+  w.out_off = 0;
+  w.max_off = align256(rows * MLA_KV_LORA_RANK * sizeof(float));
+  w.sum_off = w.max_off + align256(rows * sizeof(float));
+  w.off_off = w.sum_off + align256(rows * sizeof(float));
+  w.total = w.off_off + align256((size_t)(num_reqs + 1) * sizeof(int32_t));
+  return w;
+}
+
 struct WsLayout {
   size_t out_off, max_off, sum_off, total;
 };
-
-size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(int T, int H, int S) {
   WsLayout w;
@@ -279,10 +324,32 @@ int mla_resolve_num_segments(const mla_problem* p) {
 
 int mla_decode_workspace_bytes(const mla_problem* p, size_t* bytes) {
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = validate(p, false);
+  if (st != MLA_OK) return st;
+  if (p->num_segments == 0) {
+    const SplitPlan sp = plan_split(p, resolved_tile(p));
+    if (sp.grid_wgs > 0) {
+      *bytes = split_ws(sp, p->num_reqs).total;
+      return MLA_OK;
+    }
+  }
   const int S = mla_resolve_num_segments(p);
   if (S < 0) return S;
   *bytes = ws_layout(p->num_tokens, p->num_heads, S).total;
   return MLA_OK;
+}
+
+int mla_split_plan(const mla_problem* p, int32_t* workgroups, int32_t* rows_per_workgroup,
+                   int32_t* unit_keys) {
+  const int st = validate(p, false);
+  if (st != MLA_OK) return st;
+  if (p->num_segments != 0) return 0;
+  const SplitPlan sp = plan_split(p, resolved_tile(p));
+  if (sp.grid_wgs <= 0) return 0;
+  if (workgroups) *workgroups = sp.grid_wgs;
+  if (rows_per_workgroup) *rows_per_workgroup = sp.rows_wg;
+  if (unit_keys) *unit_keys = sp.tt;
+  return 1;
 }
 
 int mla_decode_segments(const mla_problem* p, float* segm_output, float* segm_max, float* segm_expsum,
@@ -297,7 +364,7 @@ int mla_decode_segments(const mla_problem* p, float* segm_output, float* segm_ma
   mla::SegmentLaunch a = make_launch(p, tile, p->num_segments, segm_output, segm_max, segm_expsum);
   const mla::SegmentShape sh =
       mla::segment_shape(p->kv_dtype == MLA_DTYPE_FP8_E4M3, p->num_heads, a.max_qlen, tile);
-  hipError_t e = mla::launch_segments(a, sh, static_cast<hipStream_t>(stream));
+  hipError_t e = mla::launch_segments(a, sh, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "segment kernel launch");
   return MLA_OK;
 }
@@ -341,53 +408,126 @@ int mla_merge_segments(const float* segm_output, const float* segm_max, const fl
   return MLA_OK;
 }
 
-int mla_decode(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
-               void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Both stages of the fused decode; stage 1 = the key stream, stage 2 = the
+// merge, 3 = both.
+int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
+                  void* workspace, size_t workspace_bytes, int stages, void* stream) {
   int st = validate(p, false);
   if (st != MLA_OK) return st;
   const int oc = out_code(out_dtype);
   if (oc < 0) return fail(MLA_ERR_UNSUPPORTED, "out_dtype %d not supported (bf16, fp16, fp32)", out_dtype);
+  if (stages < 1 || stages > 3) return fail(MLA_ERR_INVALID_ARG, "stages must be 1, 2 or 3, got %d", stages);
   if (p->num_tokens == 0) return MLA_OK;
   if (!out || !lse) return fail(MLA_ERR_INVALID_ARG, "out and lse must not be NULL");
   if (!aligned16(out)) return fail(MLA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  const int tile = resolved_tile(p);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+
+  if (p->num_segments == 0) {
+    const SplitPlan sp = plan_split(p, tile);
+    if (sp.grid_wgs > 0) {
+      const SplitWs w = split_ws(sp, p->num_reqs);
+      if (!workspace || workspace_bytes < w.total)
+        return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                    workspace ? workspace_bytes : (size_t)0);
+      float* so = reinterpret_cast<float*>(ws + w.out_off);
+      float* sm = reinterpret_cast<float*>(ws + w.max_off);
+      float* ss = reinterpret_cast<float*>(ws + w.sum_off);
+      int32_t* offs = reinterpret_cast<int32_t*>(ws + w.off_off);
+      if (stages & 1) {
+        mla::SegmentLaunch a = make_launch(p, tile, 1, so, sm, ss);
+        a.out = out;
+        a.out_dtype = oc;
+        a.lse = lse;
+        a.sinks = sinks;
+        a.unit_offsets = offs;
+        hipError_t e = mla::launch_segments(a, sp.sh, sp.grid_wgs, hs);
+        if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+      }
+      if (stages & 2) {
+        mla::MergeLaunch m;
+        memset(&m, 0, sizeof(m));
+        m.seg_out = so;
+        m.seg_max = sm;
+        m.seg_sum = ss;
+        m.seq_lens = p->seq_lens;
+        m.qo_indptr = p->qo_indptr;
+        m.num_reqs = p->num_reqs;
+        m.num_tokens = p->num_tokens;
+        m.num_heads = p->num_heads;
+        m.num_segments = 1;
+        m.tile = tile;
+        m.sinks = sinks;
+        m.out = out;
+        m.out_dtype = oc;
+        m.lse = lse;
+        m.unit_offsets = offs;
+        m.rows_wg = sp.rows_wg;
+        m.tt = sp.tt;
+        m.grid_wgs = sp.grid_wgs;
+        hipError_t e = mla::launch_merge(m, hs);
+        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+      }
+      return MLA_OK;
+    }
+  }
+
   const int S = mla_resolve_num_segments(p);
   if (S < 0) return S;
   const WsLayout w = ws_layout(p->num_tokens, p->num_heads, S);
   if (!workspace || workspace_bytes < w.total)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                 workspace ? workspace_bytes : (size_t)0);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  char* ws = static_cast<char*>(workspace);
   float* so = reinterpret_cast<float*>(ws + w.out_off);
   float* sm = reinterpret_cast<float*>(ws + w.max_off);
   float* ss = reinterpret_cast<float*>(ws + w.sum_off);
-  const int tile = resolved_tile(p);
-  mla::SegmentLaunch a = make_launch(p, tile, S, so, sm, ss);
-  const mla::SegmentShape sh =
-      mla::segment_shape(p->kv_dtype == MLA_DTYPE_FP8_E4M3, p->num_heads, a.max_qlen, tile);
-  hipError_t e = mla::launch_segments(a, sh, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "segment kernel launch");
-  mla::MergeLaunch m;
-  memset(&m, 0, sizeof(m));
-  m.seg_out = so;
-  m.seg_max = sm;
-  m.seg_sum = ss;
-  m.part_lens = nullptr;
-  m.seq_lens = p->seq_lens;
-  m.qo_indptr = p->qo_indptr;
-  m.num_reqs = p->num_reqs;
-  m.num_tokens = p->num_tokens;
-  m.num_heads = p->num_heads;
-  m.num_segments = S;
-  m.tile = tile;
-  m.sinks = sinks;
-  m.out = out;
-  m.out_dtype = oc;
-  m.lse = lse;
-  e = mla::launch_merge(m, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  if (stages & 1) {
+    mla::SegmentLaunch a = make_launch(p, tile, S, so, sm, ss);
+    const mla::SegmentShape sh =
+        mla::segment_shape(p->kv_dtype == MLA_DTYPE_FP8_E4M3, p->num_heads, a.max_qlen, tile);
+    hipError_t e = mla::launch_segments(a, sh, 0, hs);
+    if (e != hipSuccess) return hip_fail(e, "segment kernel launch");
+  }
+  if (stages & 2) {
+    mla::MergeLaunch m;
+    memset(&m, 0, sizeof(m));
+    m.seg_out = so;
+    m.seg_max = sm;
+    m.seg_sum = ss;
+    m.part_lens = nullptr;
+    m.seq_lens = p->seq_lens;
+    m.qo_indptr = p->qo_indptr;
+    m.num_reqs = p->num_reqs;
+    m.num_tokens = p->num_tokens;
+    m.num_heads = p->num_heads;
+    m.num_segments = S;
+    m.tile = tile;
+    m.sinks = sinks;
+    m.out = out;
+    m.out_dtype = oc;
+    m.lse = lse;
+    hipError_t e = mla::launch_merge(m, hs);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  }
   return MLA_OK;
+}
+
+}  // namespace
+
+int mla_decode(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_stages(p, sinks, out, out_dtype, lse, workspace, workspace_bytes, 3, stream);
+}
+
+int mla_decode_stage(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
+                     void* workspace, size_t workspace_bytes, int32_t stage, void* stream) {
+  if (stage != 1 && stage != 2) return fail(MLA_ERR_INVALID_ARG, "stage must be 1 or 2, got %d", stage);
+  return decode_stages(p, sinks, out, out_dtype, lse, workspace, workspace_bytes, stage, stream);
 }
 
 }  // extern "C"

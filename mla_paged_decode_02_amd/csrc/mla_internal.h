@@ -10,33 +10,36 @@ namespace mla {
 
 constexpr int kHeadDim = 576;
 constexpr int kKvRank = 512;
-// Launch shape of the segment kernel per (dtype, waves per workgroup):
+// Launch shape of the segment kernel per (dtype, waves per workgroup, 16-row
+// groups per wave):
 //  tt   tokens per LDS tile (16 for bf16 with one wave, so that a 2-slot ring
 //       of 18 KiB tiles lets four workgroups share a CU; else 32),
 //  ring LDS ring bytes per workgroup,
 //  occ  waves per SIMD the kernel's registers are sized for (2 caps a wave
-//       at 256 registers).
+//       at 256 registers; 1 allows 512, which two row groups need).
 struct ShapeCfg {
   int tt;
   int ring;
   int occ;
 };
-constexpr ShapeCfg shape_cfg(bool fp8, int waves) {
+constexpr ShapeCfg shape_cfg(bool fp8, int waves, int rg) {
   // One wave: four workgroups per CU, one wave per SIMD, 2-slot ring.
   // Four waves: two workgroups per CU (two waves per SIMD hide each other's
   // LDS and MFMA latency; measured 1.9x faster than one 144 KiB workgroup).
   // Eight waves: one workgroup, two waves per SIMD.
-  return waves == 1 ? ShapeCfg{fp8 ? 32 : 16, 36864, 1}
+  // Two row groups per wave: every LDS read feeds two MFMAs; one wave per SIMD.
+  return rg == 2 ? (waves == 2 ? ShapeCfg{32, 73728, 1} : ShapeCfg{32, 147456, 1})
+       : waves == 1 ? ShapeCfg{fp8 ? 32 : 16, 36864, 1}
        : waves == 2 ? ShapeCfg{32, 73728, 1}
        : waves == 4 ? ShapeCfg{32, 73728, 2}
                     : ShapeCfg{32, 147456, 2};
 }
-constexpr int tile_tokens(bool fp8, int waves) { return shape_cfg(fp8, waves).tt; }
+constexpr int tile_tokens(bool fp8, int waves, int rg) { return shape_cfg(fp8, waves, rg).tt; }
 // Workgroups one CU holds at once: bound by LDS and by wave slots.
-constexpr int wgs_per_cu(bool fp8, int waves) {
-  return (147456 / shape_cfg(fp8, waves).ring) < (4 * shape_cfg(fp8, waves).occ / waves)
-             ? (147456 / shape_cfg(fp8, waves).ring)
-             : (4 * shape_cfg(fp8, waves).occ / waves);
+constexpr int wgs_per_cu(bool fp8, int waves, int rg) {
+  return (147456 / shape_cfg(fp8, waves, rg).ring) < (4 * shape_cfg(fp8, waves, rg).occ / waves)
+             ? (147456 / shape_cfg(fp8, waves, rg).ring)
+             : (4 * shape_cfg(fp8, waves, rg).occ / waves);
 }
 
 struct SegmentLaunch {
@@ -57,10 +60,16 @@ struct SegmentLaunch {
   int32_t num_tokens, num_heads, num_reqs, max_qlen;
   int32_t causal, tile, num_segments;
   float softmax_scale;
-  // outputs
+  // partial outputs (segment partials, or the split kernel's piece partials)
   float* seg_out;
   float* seg_max;
   float* seg_sum;
+  // split kernel: finished rows go straight to the output
+  void* out;
+  int32_t out_dtype;  // 0 bf16, 1 fp16, 2 fp32
+  float* lse;
+  const float* sinks;     // nullable
+  int32_t* unit_offsets;  // [num_reqs + 1]: unit offset of each request, then the total
 };
 
 struct MergeLaunch {
@@ -76,6 +85,10 @@ struct MergeLaunch {
   void* out;
   int32_t out_dtype;
   float* lse;
+  // balanced split pieces (unit_offsets != NULL): rows per workgroup, tile
+  // tokens and workgroup count of the split kernel that wrote them
+  const int32_t* unit_offsets;
+  int32_t rows_wg, tt, grid_wgs;
 };
 
 // Kernel shape chosen by the host for a decode batch.
@@ -89,7 +102,9 @@ struct SegmentShape {
 
 SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile);
 
-hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, hipStream_t stream);
+// split_wgs > 0: the balanced split kernel on that many workgroups; else the
+// segment kernel on (num_segments, num_reqs, chunks).
+hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 
 }  // namespace mla

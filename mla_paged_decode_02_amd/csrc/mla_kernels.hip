@@ -152,57 +152,79 @@ __device__ __forceinline__ T lds_load(const char* base, int off) {
   return *(const LDS_AS T*)(base + off);
 }
 
-// NW waves x RG row groups of 16 rows per workgroup.
-// TT tokens per LDS tile (16 or 32; fp8 always uses 32).  OCC waves per SIMD
-// the register allocation must allow (2 caps a wave at 256 registers).
+// One piece of work for a workgroup: the query rows [row0, row0 + rows per
+// workgroup) of request r (rows are (token, head) pairs, token-major) against
+// the request's key positions [seg_start, seg_end).
+struct Piece {
+  int r, t0, qlen, L;
+  int row0;
+  int seg_start, seg_end;
+  int mode;        // kOutSegment, kOutFinal or kOutSplit
+  int s;           // segment index (kOutSegment)
+  int64_t prow0;   // first partial row of the piece (kOutSplit)
+};
+// Where a piece's result goes:
+//  segment: base-2 partials of segment s at [t, h, s] of the segment buffers;
+//  final:   the piece is a whole (request, row chunk): normalised output and
+//           natural-log LSE (sinks folded in) written directly;
+//  split:   base-2 partials at rows prow0 + local row of the split buffers.
+constexpr int kOutSegment = 0, kOutFinal = 1, kOutSplit = 2;
+
+template <bool FP8, int TT>
+struct TileGeom {
+  using F = KvFmt<FP8>;
+  static constexpr int kTileBytes = TT * F::kRowBytes;  // bf16 36864 / 18432, fp8 18432
+};
+
+__device__ __forceinline__ float logaddexp_f(float a, float b) {
+  const float mx = fmaxf(a, b);
+  return (mx == -INFINITY) ? -INFINITY : mx + log1pf(expf(-fabsf(a - b)));
+}
+
+__device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+// Streams one piece through the LDS ring and writes its result.  NW waves x
+// RG row groups of 16 rows per workgroup; TT tokens per LDS tile (16 or 32;
+// fp8 always uses 32); OCC waves per SIMD the register allocation must allow
+// (2 caps a wave at 256 registers).  Every wave of the workgroup calls it with
+// the same piece (it holds workgroup barriers).
 template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void segment_kernel(
-    SegmentLaunch p) {
+__device__ __forceinline__ void run_piece(const SegmentLaunch& p,
+                                          char (*lds)[TileGeom<FP8, TT>::kTileBytes],
+                                          int* phys_rows, const Piece& pc) {
   using F = KvFmt<FP8>;
   static_assert(TT == 32 || (TT == 16 && !FP8), "tile shape");
   constexpr int kNB = TT / 16;                         // 16-token blocks per tile
   constexpr int kRowBytes = F::kRowBytes;
   constexpr int kVRegion = TT * F::kVPitch;
-  constexpr int kTileBytes = TT * kRowBytes;           // bf16 36864 / 18432, fp8 18432
+  constexpr int kTileBytes = TT * kRowBytes;
   constexpr int kRowsPerV = 1024 / F::kVPitch;         // rows per V-region DMA instruction
   constexpr int kNIV = TT / kRowsPerV;                 // V-region DMA instructions
   constexpr int kNI = kTileBytes / 1024;               // all DMA instructions per tile
   constexpr int kNIw = kNIV / NW + (kNI - kNIV) / NW;   // per wave, lower bound
   constexpr int kRowsWG = 16 * RG * NW;
   static_assert(kTileBytes % 1024 == 0, "tile must be whole DMA instructions");
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF][kTileBytes];
-  __shared__ int phys_rows[CONTIG ? 1 : TT];
 
-  const int s = blockIdx.x;
-  const int r = blockIdx.y;
-  const int chunk = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int g = lane >> 4;
   const int n = lane & 15;
 
-  // ---- request geometry (uniform over the workgroup) ----
-  int t0 = r, qlen = 1;
-  if (p.qo_indptr) {
-    t0 = p.qo_indptr[r];
-    qlen = p.qo_indptr[r + 1] - t0;
-    if (t0 < 0 || qlen < 0 || qlen > p.max_qlen || t0 + qlen > p.num_tokens) return;
-  }
+  const int r = pc.r, t0 = pc.t0, qlen = pc.qlen, L = pc.L;
   const int H = p.num_heads;
   const int M = qlen * H;
-  const int row0 = chunk * kRowsWG;
-  if (row0 >= M) return;
-
-  const int L = p.seq_lens[r];
-  if (L <= 0) return;  // no valid segment
+  const int row0 = pc.row0;
   // A length past the block table is reported as NaN; rows beyond the table
   // are never read.
   const int cap = p.bt_cols * p.block_size;
   bool bad = L > cap;
-  const int span = cdiv(L, p.num_segments * p.tile) * p.tile;
-  const int seg_start = s * span;
-  if (seg_start >= L) return;  // invalid segment: its slot is never read
-  const int seg_end = min(seg_start + span, L);
+  const int seg_start = pc.seg_start;
+  const int seg_end = pc.seg_end;
 
   // The workgroup's last row decides how far its rows can see.
   const int last_row = min(row0 + kRowsWG, M) - 1;
@@ -632,43 +654,262 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
     }
   }
 
-  // ---- write this segment's partials ----
+  // ---- write the piece's result ----
   bad = __syncthreads_or(bad ? 1 : 0) != 0;
 #pragma unroll
   for (int q = 0; q < RG; ++q) {
     float l_tot = l_run[q] + __shfl_xor(l_run[q], 16);
     l_tot += __shfl_xor(l_tot, 32);
     if (!rok[q]) continue;
-    const int64_t slot = ((int64_t)(t0 + ti[q]) * H + hh[q]) * p.num_segments + s;
-    float* outp = p.seg_out + slot * kKvRank + 4 * g;
+    // One store loop for every destination: values acc * mult, as fp32 or
+    // as 16-bit (bf16 rounded to nearest even, or fp16).
+    float mult, stat0, stat1;
+    float* stat0_p;
+    float* stat1_p;
+    char* dst;
+    int kind;  // 0 bf16, 1 fp16, 2 fp32
+    if (pc.mode == kOutFinal) {
+      // Normalised output and natural-log LSE; an optional sink joins the
+      // softmax as one more logit with a zero value.
+      const bool has = m_true[q] > -INFINITY;
+      float lse = has ? kLn2 * (m_true[q] + __log2f(l_tot)) : -INFINITY;
+      mult = has ? ks / l_tot : 0.f;
+      if (p.sinks) {
+        const float nl = logaddexp_f(lse, p.sinks[hh[q]]);
+        mult = has ? mult * expf(lse - nl) : 0.f;
+        lse = nl;
+      }
+      if (bad) { lse = __builtin_nanf(""); mult = __builtin_nanf(""); }
+      const int64_t orow = (int64_t)(t0 + ti[q]) * H + hh[q];
+      kind = p.out_dtype;
+      dst = (char*)p.out + (orow * kKvRank + 4 * g) * (kind == 2 ? 4 : 2);
+      stat0 = lse;
+      stat0_p = p.lse + orow;
+      stat1 = 0.f;
+      stat1_p = nullptr;
+    } else {
+      const int64_t slot = pc.mode == kOutSegment
+                               ? ((int64_t)(t0 + ti[q]) * H + hh[q]) * p.num_segments + pc.s
+                               : pc.prow0 + (wave * RG + q) * 16 + n;
+      mult = ks;
+      kind = 2;
+      dst = (char*)(p.seg_out + slot * kKvRank + 4 * g);
+      stat0 = bad ? __builtin_nanf("") : m_true[q];
+      stat0_p = p.seg_max + slot;
+      stat1 = l_tot;
+      stat1_p = p.seg_sum + slot;
+    }
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
-      *(f32x4*)(outp + 16 * db) = acc[q][db] * ks;
+      const f32x4 o = acc[q][db] * mult;
+      if (kind == 2) {
+        *(f32x4*)(dst + 64 * db) = o;
+      } else {
+        u32x2 v;
+        if (kind == 0) {
+          v[0] = (unsigned)f32_to_bf16_rne(o[0]) | ((unsigned)f32_to_bf16_rne(o[1]) << 16);
+          v[1] = (unsigned)f32_to_bf16_rne(o[2]) | ((unsigned)f32_to_bf16_rne(o[3]) << 16);
+        } else {
+          v[0] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[0]) |
+                 ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[1]) << 16);
+          v[1] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[2]) |
+                 ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[3]) << 16);
+        }
+        *(u32x2*)(dst + 32 * db) = v;
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (g == 0) {
-      p.seg_max[slot] = bad ? __builtin_nanf("") : m_true[q];
-      p.seg_sum[slot] = l_tot;
+      *stat0_p = stat0;
+      if (stat1_p) *stat1_p = stat1;
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// Merge kernel: one wave per (token, head); lane covers dims [8*lane, 8*lane+8).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
-  unsigned u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
+// Segment kernel: one workgroup per (segment, request, row chunk); the key
+// partition is the segment formula of the merge page's module description
+// (span = cdiv(len, S * TILE) * TILE; segment s = [s * span, min((s+1) * span, len))).
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void segment_kernel(
+    SegmentLaunch p) {
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][TileGeom<FP8, TT>::kTileBytes];
+  __shared__ int phys_rows[CONTIG ? 1 : TT];
+  constexpr int kRowsWG = 16 * RG * NW;
+  const int s = blockIdx.x;
+  const int r = blockIdx.y;
+  const int chunk = blockIdx.z;
+  int t0 = r, qlen = 1;
+  if (p.qo_indptr) {
+    t0 = p.qo_indptr[r];
+    qlen = p.qo_indptr[r + 1] - t0;
+    if (t0 < 0 || qlen < 0 || qlen > p.max_qlen || t0 + qlen > p.num_tokens) return;
+  }
+  const int row0 = chunk * kRowsWG;
+  if (row0 >= qlen * p.num_heads) return;
+  const int L = p.seq_lens[r];
+  if (L <= 0) return;  // no valid segment
+  const int span = cdiv(L, p.num_segments * p.tile) * p.tile;
+  const int seg_start = s * span;
+  if (seg_start >= L) return;  // invalid segment: its slot is never read
+  Piece pc;
+  pc.r = r; pc.t0 = t0; pc.qlen = qlen; pc.L = L; pc.row0 = row0;
+  pc.seg_start = seg_start; pc.seg_end = min(seg_start + span, L);
+  pc.mode = kOutSegment; pc.s = s; pc.prow0 = 0;
+  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC>(p, lds, phys_rows, pc);
 }
 
-// One wave per (token, head) row; lane covers dims [8*lane, 8*lane+8).  The
-// valid segments' statistics are read one per lane (up to 64 at a time), the
-// weights 2^(m_s - M) broadcast from the owning lane, and the partial rows
-// streamed with several loads in flight.
-template <int OUT>  // 0 bf16, 1 fp16, 2 fp32
+// Work units of request r for a workgroup shape of rows_wg rows and TT-token
+// tiles: (row chunks) x (tiles of its keys).  0 for an empty or malformed
+// request (the merge writes its empty rows).
+__device__ __forceinline__ int request_units(const SegmentLaunch& p, int r, int rows_wg, int tt, int* t0_out,
+                                             int* qlen_out, int* len_out) {
+  int t0 = r, qlen = 1;
+  if (p.qo_indptr) {
+    t0 = p.qo_indptr[r];
+    qlen = p.qo_indptr[r + 1] - t0;
+  }
+  const int L = p.seq_lens[r];
+  *t0_out = t0; *qlen_out = qlen; *len_out = L;
+  if (t0 < 0 || qlen <= 0 || qlen > p.max_qlen || t0 + qlen > p.num_tokens || L <= 0) return 0;
+  return cdiv(qlen * p.num_heads, rows_wg) * cdiv(L, tt);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Balanced split kernel (the fused decode's first stage).  The work of the
+// whole batch is laid out as one sequence of units, request by request, row
+// chunk by row chunk, tile by tile; workgroup g of G takes units
+// [g W / G, (g+1) W / G), so every workgroup streams the same number of tiles
+// whatever the lengths.  A (request, row chunk) whose tiles all fall in one
+// workgroup is finished there (output and LSE written); one cut by a range
+// boundary leaves base-2 partials in the workgroup's slot 0 (its first piece)
+// or slot 1 (its last piece) for the merge.  Workgroup 0 also stores the
+// per-request unit offsets the merge uses to find the pieces.
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void split_kernel(
+    SegmentLaunch p) {
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][TileGeom<FP8, TT>::kTileBytes];
+  __shared__ int phys_rows[CONTIG ? 1 : TT];
+  constexpr int kRowsWG = 16 * RG * NW;
+  const int lane = threadIdx.x & 63;
+  const int R = p.num_reqs;
+  const int G = gridDim.x;
+  const int gw = blockIdx.x;
+
+  // Total units W (every wave computes the same values).
+  int W = 0;
+  for (int i = 0; i < R; i += 64) {
+    int t0, ql, L;
+    const int u = (i + lane < R) ? request_units(p, i + lane, kRowsWG, TT, &t0, &ql, &L) : 0;
+    W += __shfl(wave_incl_scan(u), 63);
+  }
+  // Lane shuffles read as divergent to the compiler: make the uniform values
+  // scalar so the tile loop's geometry stays in scalar registers.
+  W = __builtin_amdgcn_readfirstlane(W);
+  const int64_t s_g = ((int64_t)gw * W) / G;
+  const int64_t e_g = ((int64_t)(gw + 1) * W) / G;
+
+  // First request whose units reach past s_g, and its unit offset; workgroup 0
+  // records every offset (and W) for the merge.
+  int r = -1;
+  int base = 0;
+  int carry = 0;
+  for (int i = 0; i < R; i += 64) {
+    int t0, ql, L;
+    const int u = (i + lane < R) ? request_units(p, i + lane, kRowsWG, TT, &t0, &ql, &L) : 0;
+    const int incl = wave_incl_scan(u);
+    const int excl = carry + incl - u;
+    if (gw == 0 && threadIdx.x < 64 && i + lane < R) p.unit_offsets[i + lane] = excl;
+    if (r < 0) {
+      const unsigned long long hit = __ballot(u > 0 && excl <= s_g && s_g < (int64_t)excl + u);
+      if (hit) {
+        const int j = __builtin_ctzll(hit);
+        r = i + j;
+        base = __shfl(excl, j);
+      }
+    }
+    carry = __builtin_amdgcn_readfirstlane(carry + __shfl(incl, 63));
+  }
+  if (gw == 0 && threadIdx.x == 0) p.unit_offsets[R] = W;
+  r = __builtin_amdgcn_readfirstlane(r);
+  base = __builtin_amdgcn_readfirstlane(base);
+  if (s_g >= e_g || r < 0) return;
+
+  int64_t pos = s_g;
+  while (pos < e_g && r < R) {
+    int t0, qlen, L;
+    const int units = request_units(p, r, kRowsWG, TT, &t0, &qlen, &L);
+    if (pos >= base + units) {  // past this request (or it has no units)
+      base += units;
+      ++r;
+      continue;
+    }
+    const int nt = cdiv(L, TT);
+    const int local = (int)(pos - base);
+    const int c = local / nt;
+    const int a = local - c * nt;
+    const int b = (int)min((int64_t)nt, (int64_t)a + (e_g - pos));
+    Piece pc;
+    pc.r = r; pc.t0 = t0; pc.qlen = qlen; pc.L = L;
+    pc.row0 = c * kRowsWG;
+    pc.seg_start = a * TT;
+    pc.seg_end = min(b * TT, L);
+    pc.mode = (a == 0 && b == nt) ? kOutFinal : kOutSplit;
+    pc.s = 0;
+    pc.prow0 = ((int64_t)gw * 2 + (pos == s_g ? 0 : 1)) * kRowsWG;
+    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC>(p, lds, phys_rows, pc);
+    pos += b - a;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge kernel
+// ---------------------------------------------------------------------------
+// Request of token t: the largest r with qo_indptr[r] <= t, found 64 entries
+// at a time (one load per lane and a ballot per level: one level for fewer
+// than 64 requests, two below 4096).
+__device__ __forceinline__ int request_of_token(const int32_t* qo_indptr, int num_reqs, int t) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, span = num_reqs + 1;
+  while (span > 1) {
+    const int step = cdiv(span, 64);
+    const int idx = lo + lane * step;
+    const bool ok = lane * step < span && qo_indptr[idx] <= t;
+    const unsigned long long mask = __ballot(ok);
+    const int j = mask ? 63 - __builtin_clzll(mask) : 0;
+    lo += j * step;
+    span = min(step, num_reqs + 1 - lo);
+  }
+  return min(lo, num_reqs - 1);
+}
+
+// Merge kernel: one wave per (token, head) row; lane covers dims
+// [8 lane, 8 lane + 8).  The row's piece statistics (one piece per lane) and
+// the data of its first 16 pieces are loaded together; the weights
+// 2^(m_i - M) follow once the statistics are in, and longer rows stream
+// further blocks of 16 pieces.
+//
+// Segment pieces (SPLIT false): the valid segments of part_lens[t] (or of the
+// token's request length), contiguous at [t, h, 0..nv).
+// SPLIT: the pieces are those of the balanced split kernel.  The row's
+// (request, row chunk) covers units [P, P + nt) of the batch's unit sequence;
+// the workgroups g_first..g_last holding them left partials in slot 1 of
+// g_first when that workgroup began before P, else in slot 0.  With more
+// workgroups than units some ranges are empty; those wrote nothing and are
+// skipped.  A row whose units all fell in one workgroup was finished there and
+// is skipped here; an empty row gets O = 0 and LSE = -inf (or its sink).
+template <int OUT, bool SPLIT>  // OUT: 0 bf16, 1 fp16, 2 fp32
 __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
+  constexpr int kBlk = 16;  // pieces in flight per step
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (int64_t)p.num_tokens * p.num_heads) return;
@@ -676,65 +917,131 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
   const int h = (int)(row - (int64_t)t * p.num_heads);
   const int S = p.num_segments;
 
-  int L;
-  if (p.part_lens) {
-    L = p.part_lens[t];
-  } else if (p.qo_indptr) {
-    // request of token t: largest r with qo_indptr[r] <= t
-    int lo = 0, hi = p.num_reqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.qo_indptr[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    L = p.seq_lens[lo];
-  } else {
-    L = p.seq_lens[t];
-  }
+  int req = t;
+  if ((SPLIT || !p.part_lens) && p.qo_indptr) req = request_of_token(p.qo_indptr, p.num_reqs, t);
   int nv = 0;
-  if (L > 0) {
-    const int span = cdiv(L, S * p.tile) * p.tile;
-    nv = min(S, cdiv(L, span));
-  }
   const int64_t base = row * S;
-
-  // Pass 1: global max M, error flag, and L = sum l_s 2^(m_s - M).
-  float M = -INFINITY;
-  bool nan_seen = false;
-  for (int s0 = 0; s0 < nv; s0 += 64) {
-    const int s = s0 + lane;
-    const float m = s < nv ? p.seg_max[base + s] : -INFINITY;
-    nan_seen |= (m != m);
-    M = fmaxf(M, m);
+  int64_t row_i0 = 0, first_row = 0, stride = 0, gf = 0, W = 1, G = 1;
+  if constexpr (SPLIT) {
+    const int t0 = p.qo_indptr ? p.qo_indptr[req] : req;
+    const int qlen = p.qo_indptr ? p.qo_indptr[req + 1] - t0 : 1;
+    const int rr = (t - t0) * p.num_heads + h;  // row within the request
+    const int c = rr / p.rows_wg, local = rr - c * p.rows_wg;
+    const int units = p.unit_offsets[req + 1] - p.unit_offsets[req];
+    W = p.unit_offsets[p.num_reqs];
+    const int chunks = cdiv(qlen * p.num_heads, p.rows_wg);
+    const int nt = units > 0 ? units / chunks : 0;
+    if (nt > 0 && W > 0) {
+      const int64_t P = (int64_t)p.unit_offsets[req] + (int64_t)c * nt;
+      G = p.grid_wgs;
+      gf = ((P + 1) * G - 1) / W;
+      const int64_t gl = ((P + nt) * G - 1) / W;
+      if (gf == gl) return;  // finished by the split kernel
+      nv = (int)(gl - gf + 1);
+      const int64_t start_f = (gf * W) / G;
+      row_i0 = (gf * 2 + (start_f < P ? 1 : 0)) * p.rows_wg + local;
+      first_row = (gf * 2) * p.rows_wg + local;
+      stride = 2 * p.rows_wg;
+    }
+  } else {
+    const int L = p.part_lens ? p.part_lens[t] : p.seq_lens[req];
+    if (L > 0) {
+      const int span = cdiv(L, S * p.tile) * p.tile;
+      nv = min(S, cdiv(L, span));
+    }
   }
+  // Row index of piece i in the partial buffers, and whether it exists.
+  auto prow = [&](int i) -> int64_t {
+    if constexpr (SPLIT) return i == 0 ? row_i0 : first_row + (int64_t)i * stride;
+    return base + i;
+  };
+  auto present = [&](int i) -> bool {
+    if constexpr (SPLIT) {
+      const int64_t g = gf + i;
+      return ((g + 1) * W) / G > (g * W) / G;
+    }
+    return true;
+  };
+  auto load_block = [&](f32x4 (&v)[2 * kBlk], int j0, unsigned long long pmask, int cnt) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  nan_seen = __ballot(nan_seen) != 0;
-  const bool has = M > -INFINITY;
+    for (int u = 0; u < kBlk; ++u) {
+      if (j0 + u < cnt && ((pmask >> (j0 + u)) & 1ull)) {
+        const float* src = p.seg_out + prow(j0 + u) * kKvRank + 8 * lane;
+        v[2 * u] = *(const f32x4*)(src);
+        v[2 * u + 1] = *(const f32x4*)(src + 4);
+      } else {
+        v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float Lsum = 0.f;
-  if (has) {
+  float M = -INFINITY, Lsum = 0.f;
+  bool nan_seen = false;
+  if (nv <= 64) {
+    // Common case: statistics of every piece in one load per lane, issued with
+    // the first block's data.
+    const bool pres = lane < nv && present(lane);
+    const unsigned long long pmask = __ballot(pres);
+    const float m = pres ? p.seg_max[prow(lane)] : -INFINITY;
+    const float l = pres ? p.seg_sum[prow(lane)] : 0.f;
+    f32x4 v[2 * kBlk];
+    load_block(v, 0, pmask, nv);
+    nan_seen = __ballot(m != m) != 0;
+    M = m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float wgt = (m > -INFINITY) ? exp2f(m - M) : 0.f;
+    Lsum = l * wgt;
+    for (int j0 = 0; j0 < nv; j0 += kBlk) {
+      if (j0 > 0) load_block(v, j0, pmask, nv);
+#pragma unroll
+      for (int u = 0; u < kBlk; ++u) {
+        const float wu = __shfl(wgt, (j0 + u) & 63);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += wu * v[2 * u][e];
+          acc[4 + e] += wu * v[2 * u + 1][e];
+        }
+      }
+    }
+  } else {
+    // Long rows: the maximum first, then blocks of 64 pieces.
     for (int s0 = 0; s0 < nv; s0 += 64) {
-      const int s = s0 + lane;
+      const int i = s0 + lane;
+      const float m = (i < nv && present(i)) ? p.seg_max[prow(i)] : -INFINITY;
+      nan_seen |= (m != m);
+      M = fmaxf(M, m);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    nan_seen = __ballot(nan_seen) != 0;
+    for (int s0 = 0; s0 < nv; s0 += 64) {
+      const int i = s0 + lane;
+      const bool pres = i < nv && present(i);
+      const unsigned long long pmask = __ballot(pres);
       float wgt = 0.f;
-      if (s < nv) {
-        const float m = p.seg_max[base + s];
+      if (pres) {
+        const float m = p.seg_max[prow(i)];
         wgt = (m > -INFINITY) ? exp2f(m - M) : 0.f;
-        Lsum += p.seg_sum[base + s] * wgt;
+        Lsum += p.seg_sum[prow(i)] * wgt;
       }
       const int cnt = min(64, nv - s0);
-      const float* src = p.seg_out + (base + s0) * kKvRank + 8 * lane;
-      int j = 0;
-      for (; j + 4 <= cnt; j += 4) {
-        f32x4 v[8];
+      for (int j0 = 0; j0 < cnt; j0 += kBlk) {
+        f32x4 v[2 * kBlk];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          v[2 * u] = *(const f32x4*)(src + (j + u) * kKvRank);
-          v[2 * u + 1] = *(const f32x4*)(src + (j + u) * kKvRank + 4);
+        for (int u = 0; u < kBlk; ++u) {
+          if (j0 + u < cnt && ((pmask >> (j0 + u)) & 1ull)) {
+            const float* src = p.seg_out + prow(s0 + j0 + u) * kKvRank + 8 * lane;
+            v[2 * u] = *(const f32x4*)(src);
+            v[2 * u + 1] = *(const f32x4*)(src + 4);
+          } else {
+            v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float wu = __shfl(wgt, j + u);
+        for (int u = 0; u < kBlk; ++u) {
+          const float wu = __shfl(wgt, (j0 + u) & 63);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             acc[e] += wu * v[2 * u][e];
@@ -742,22 +1049,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
           }
         }
       }
-      for (; j < cnt; ++j) {
-        const f32x4 a = *(const f32x4*)(src + j * kKvRank);
-        const f32x4 b = *(const f32x4*)(src + j * kKvRank + 4);
-        const float wu = __shfl(wgt, j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] += wu * a[e];
-          acc[4 + e] += wu * b[e];
-        }
-      }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) Lsum += __shfl_xor(Lsum, o);
   }
-  float lse;
-  float scale;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) Lsum += __shfl_xor(Lsum, o);
+  const bool has = M > -INFINITY;
+  float lse, scale;
   if (has) {
     lse = kLn2 * (M + log2f(Lsum));
     scale = 1.0f / Lsum;
@@ -766,9 +1063,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
     scale = 0.f;
   }
   if (p.sinks) {
-    const float sg = p.sinks[h];
-    const float mx = fmaxf(lse, sg);
-    const float nl = (mx == -INFINITY) ? -INFINITY : mx + log1pf(expf(-fabsf(lse - sg)));
+    const float nl = logaddexp_f(lse, p.sinks[h]);
     scale = has ? scale * expf(lse - nl) : 0.f;
     lse = nl;
   }
@@ -805,7 +1100,7 @@ hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
   // LDS ring per workgroup: 36 KiB with 1 wave (four workgroups per CU; bf16
   // uses 16-token tiles there), 72 KiB with 2 waves (two per CU), 144 KiB
   // with 4 waves (one per CU).
-  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW);
+  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG);
   constexpr int kTT = kCfg.tt;
   constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
   constexpr int kRing = kCfg.ring / kTileBytes;
@@ -815,13 +1110,34 @@ hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool FP8, int NW, int RG, bool CONTIG>
+hipError_t launch_split(const SegmentLaunch& a, int grid_wgs, hipStream_t stream) {
+  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG);
+  constexpr int kTT = kCfg.tt;
+  constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
+  constexpr int kRing = kCfg.ring / kTileBytes;
+  hipLaunchKernelGGL((split_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ>), dim3(grid_wgs), dim3(64 * NW), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <bool FP8, int NW, int RG, bool CONTIG>
+hipError_t launch_any(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
+  return split_wgs > 0 ? launch_split<FP8, NW, RG, CONTIG>(a, split_wgs, stream)
+                       : launch_seg<FP8, NW, RG, CONTIG>(a, sh.chunks, stream);
+}
+
 template <bool FP8, bool CONTIG>
-hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, hipStream_t stream) {
+hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
+  if (sh.rows_per_wave == 2) {
+    return sh.waves == 2 ? launch_any<FP8, 2, 2, CONTIG>(a, sh, split_wgs, stream)
+                         : launch_any<FP8, 4, 2, CONTIG>(a, sh, split_wgs, stream);
+  }
   switch (sh.waves) {
-    case 1: return launch_seg<FP8, 1, 1, CONTIG>(a, sh.chunks, stream);
-    case 2: return launch_seg<FP8, 2, 1, CONTIG>(a, sh.chunks, stream);
-    case 4: return launch_seg<FP8, 4, 1, CONTIG>(a, sh.chunks, stream);
-    default: return launch_seg<FP8, 8, 1, CONTIG>(a, sh.chunks, stream);
+    case 1: return launch_any<FP8, 1, 1, CONTIG>(a, sh, split_wgs, stream);
+    case 2: return launch_any<FP8, 2, 1, CONTIG>(a, sh, split_wgs, stream);
+    case 4: return launch_any<FP8, 4, 1, CONTIG>(a, sh, split_wgs, stream);
+    default: return launch_any<FP8, 8, 1, CONTIG>(a, sh, split_wgs, stream);
   }
 }
 
@@ -838,25 +1154,33 @@ SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
   else                  { sh.waves = 8; sh.rows_per_wave = 1; }
   const int per_wg = sh.waves * sh.rows_per_wave;
   sh.chunks = (groups + per_wg - 1) / per_wg;
-  sh.contig = tile >= tile_tokens(fp8, sh.waves);
+  sh.contig = tile >= tile_tokens(fp8, sh.waves, sh.rows_per_wave);
   return sh;
 }
 
-hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, hipStream_t stream) {
+hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
   if (sh.fp8) {
-    return sh.contig ? launch_seg_shape<true, true>(a, sh, stream) : launch_seg_shape<true, false>(a, sh, stream);
+    return sh.contig ? launch_seg_shape<true, true>(a, sh, split_wgs, stream)
+                     : launch_seg_shape<true, false>(a, sh, split_wgs, stream);
   }
-  return sh.contig ? launch_seg_shape<false, true>(a, sh, stream) : launch_seg_shape<false, false>(a, sh, stream);
+  return sh.contig ? launch_seg_shape<false, true>(a, sh, split_wgs, stream)
+                   : launch_seg_shape<false, false>(a, sh, split_wgs, stream);
+}
+
+template <bool SPLIT>
+void launch_merge_t(const MergeLaunch& a, dim3 grid, hipStream_t stream) {
+  switch (a.out_dtype) {
+    case 0: hipLaunchKernelGGL((merge_kernel<0, SPLIT>), grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((merge_kernel<1, SPLIT>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((merge_kernel<2, SPLIT>), grid, dim3(256), 0, stream, a); break;
+  }
 }
 
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_tokens * a.num_heads;
   dim3 grid((unsigned)((rows + 3) / 4));
-  switch (a.out_dtype) {
-    case 0: hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, a); break;
-    case 1: hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, stream, a); break;
-  }
+  if (a.unit_offsets) launch_merge_t<true>(a, grid, stream);
+  else launch_merge_t<false>(a, grid, stream);
   return hipGetLastError();
 }
 

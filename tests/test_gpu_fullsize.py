@@ -2,11 +2,11 @@
 
 Each workload is built at its real shape (52 requests x 16384 tokens, or the
 128-request ragged causal batch) and decoded on the GPU with the planner's
-segment count through one prepared ``mla_decode`` call, bf16 output — the
-same call ``bench.py`` times.  The fp64 oracle then computes a sample of the
+default split through one prepared ``mla_decode`` call, bf16 output (the
+same call ``bench.py`` times).  The fp64 oracle then computes a sample of the
 requests one by one, and the outputs of every token row of those requests are
 compared at the decode tolerances.  The segment partials of the same sample
-are checked too, with the same segment count.
+are checked too, with the planner's segment count.
 """
 from __future__ import annotations
 
@@ -60,7 +60,9 @@ def test_fullsize_sampled_parity(name):
     dec = m.Decoder(**args, sinks=d["sinks"], num_segments=0, out_dtype=torch.bfloat16)
     out, lse = dec.run()
     torch.cuda.synchronize()
-    S = dec.num_segments
+    # The segment partition the planner picks for the same batch (the fused
+    # call itself uses the balanced split when dec.split is set).
+    S = dec.num_segments or m.resolve_num_segments(m.make_problem(**args))
     out = out.float().cpu().numpy().astype(np.float64)
     lse = lse.cpu().numpy().astype(np.float64)
     assert np.isfinite(out).all()
@@ -70,7 +72,8 @@ def test_fullsize_sampled_parity(name):
     ref_o, ref_l = orc.mla_decode(w, reqs, db)
     tok = _tokens(w, reqs)
     err_o, err_l = assert_close(w, out, lse, ref_o, ref_l, reqs=reqs, tok=tok)
-    print(f"[fullsize] {name}: S={S} reqs={reqs} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+    print(f"[fullsize] {name}: split={dec.split} S={S} reqs={reqs} max|dO|={err_o:.3e} "
+          f"max|dLSE|={err_l:.3e}", flush=True)
 
     # Segment partials of the same sample, same segment count and tile.
     tile = w.tile_size or m.tile_size_for_block(w.block_size)

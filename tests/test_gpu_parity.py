@@ -237,3 +237,86 @@ def test_prepared_decoder_matches_decode():
         o2, l2 = dec.run()
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------- balanced split (S = 0) ----
+# mla_decode with num_segments == 0 cuts the batch's units (request, row chunk,
+# tile) into equal workgroup ranges.  max_workgroups forces few workgroups so
+# that ranges hold several whole requests, start or end inside one, or lie
+# inside one; the default uses every slot of the device.
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"{c[0]}-H{c[1]}-blk{c[2]}-q{c[4] is not None}")
+@pytest.mark.parametrize("wgs", [0, 1, 3, 7])
+def test_split_parity_sweep(case, wgs):
+    import mla_paged_decode_02_amd as m
+    dtype, H, block, lens, qlens, causal, sinks, _ = case
+    _print_case(f"split wgs={wgs} {case}")
+    w = mi.make_workload(name="split", seq_lens=lens, num_heads=H, block_size=block, dtype=dtype,
+                         qlens=qlens, causal=causal, sinks=sinks,
+                         seed=1000 * H + block + (7 if dtype == "bf16" else 0))
+    ref_o, ref_l = orc.mla_decode(w)
+    d = mi.to_torch(w, "cuda")
+    args = mi.call_args(w, d)
+    out, lse = m.decode(**args, sinks=d["sinks"], num_segments=0, max_workgroups=wgs,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                 ref_o, ref_l)
+
+
+@pytest.mark.parametrize("wgs", [0, 2, 5, 13])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_split_counts_every_key_once(dtype, wgs):
+    """q = 0 and V = bits of (position, request): every key weighs 1, so the
+    output is the exact per-bit mean and LSE = ln(len); a key dropped or seen
+    twice by the split moves them by >= 1/len."""
+    import mla_paged_decode_02_amd as m
+    lens = [1, 15, 16, 17, 100, 333, 1024, 1500]
+    w = mi.make_workload(name="split-bits", seq_lens=lens, num_heads=4, block_size=16,
+                         dtype=dtype, seed=91, qlens=[1, 2, 1, 3, 1, 1, 2, 1], causal=True)
+    w.q[:] = 0
+    flat = w.kv_cache.reshape(-1, 576)
+    one = 0x3F80 if dtype == "bf16" else 0x38  # 1.0 in bf16 / e4m3
+    for r, L in enumerate(lens):
+        for j in range(L):
+            row = orc.cache_row_index(w.block_table[r], j, w.block_size)
+            bits = [(j >> b) & 1 for b in range(11)] + [(r >> b) & 1 for b in range(3)]
+            flat[row, :] = 0
+            flat[row, :14] = [one * x for x in bits]
+    w = mi.with_(w, kv_scale=None if dtype == "bf16" else 1.0, q_scale=None if dtype == "bf16" else 1.0)
+    d = mi.to_torch(w, "cuda")
+    out, lse = m.decode(**mi.call_args(w, d), num_segments=0, max_workgroups=wgs, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qo = w.qo_indptr
+    for r, L in enumerate(lens):
+        ql = qo[r + 1] - qo[r]
+        for i in range(ql):
+            n = L - ql + i + 1
+            t = qo[r] + i
+            exp_o = [np.mean([(j >> b) & 1 for j in range(n)]) for b in range(11)] + \
+                    [float((r >> b) & 1) for b in range(3)]
+            assert np.allclose(out[t, :, :14], np.array(exp_o)[None], atol=2e-6, rtol=0), (r, i)
+            assert np.all(out[t, :, 14:] == 0)
+            assert np.allclose(lse[t], math.log(n), atol=2e-6, rtol=0), (r, i)
+
+
+def test_split_stages_and_decoder():
+    """The two stages run separately equal one mla_decode call, and a
+    prepared split decoder repeats the same bits."""
+    import mla_paged_decode_02_amd as m
+    w = mi.make_workload(name="stages", seq_lens=[3000, 64, 700, 1], num_heads=32, block_size=64,
+                         dtype="fp8_e4m3", sinks=True, seed=101)
+    d = mi.to_torch(w, "cuda")
+    args = mi.call_args(w, d)
+    o1, l1 = m.decode(**args, sinks=d["sinks"], num_segments=0)
+    dec = m.Decoder(**args, sinks=d["sinks"], num_segments=0)
+    assert dec.split_workgroups > 0 and dec.num_segments == 0
+    for _ in range(3):
+        dec.run_stage(1)
+        o2, l2 = dec.run_stage(2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ref_o, ref_l = orc.mla_decode(w)
+    assert_close(w, o1.float().cpu().numpy().astype(np.float64), l1.cpu().numpy().astype(np.float64),
+                 ref_o, ref_l)
