@@ -12,8 +12,8 @@ constexpr int kHeadDim = 576;
 constexpr int kKvRank = 512;
 // Launch shape of the segment kernel per (dtype, waves per workgroup, 16-row
 // groups per wave):
-//  tt   tokens per LDS tile (16 for bf16 with one wave, so that a 2-slot ring
-//       of 18 KiB tiles lets four workgroups share a CU; else 32),
+//  tt   tokens per LDS tile (16 for bf16 with one or four waves: 18 KiB
+//       tiles, so a ring holds enough of them in flight; else 32),
 //  ring LDS ring bytes per workgroup,
 //  occ  waves per SIMD the kernel's registers are sized for (2 caps a wave
 //       at 256 registers; 1 allows 512, which two row groups need).
@@ -22,24 +22,27 @@ struct ShapeCfg {
   int ring;
   int occ;
 };
-constexpr ShapeCfg shape_cfg(bool fp8, int waves, int rg) {
+constexpr ShapeCfg shape_cfg(bool fp8, int waves, int rg, bool ws) {
   // One wave: four workgroups per CU, one wave per SIMD, 2-slot ring.
   // Four waves: two workgroups per CU (two waves per SIMD hide each other's
   // LDS and MFMA latency; measured 1.9x faster than one 144 KiB workgroup).
   // Eight waves: one workgroup, two waves per SIMD.
   // Two row groups per wave: every LDS read feeds two MFMAs; one wave per SIMD.
-  return rg == 2 ? (waves == 2 ? ShapeCfg{32, 73728, 1} : ShapeCfg{32, 147456, 1})
+  // Specialised waves (S waves and P.V waves in pairs): one workgroup per CU,
+  // an 8-slot ring of 18 KiB tiles (fp8 32 tokens, bf16 16 tokens).
+  return ws ? ShapeCfg{fp8 ? 32 : 16, 147456, 2}
+       : rg == 2 ? (waves == 2 ? ShapeCfg{32, 73728, 1} : ShapeCfg{32, 147456, 1})
        : waves == 1 ? ShapeCfg{fp8 ? 32 : 16, 36864, 1}
        : waves == 2 ? ShapeCfg{32, 73728, 1}
-       : waves == 4 ? ShapeCfg{32, 73728, 2}
+       : waves == 4 ? ShapeCfg{fp8 ? 32 : 16, 73728, 2}
                     : ShapeCfg{32, 147456, 2};
 }
-constexpr int tile_tokens(bool fp8, int waves, int rg) { return shape_cfg(fp8, waves, rg).tt; }
+constexpr int tile_tokens(bool fp8, int waves, int rg, bool ws) { return shape_cfg(fp8, waves, rg, ws).tt; }
 // Workgroups one CU holds at once: bound by LDS and by wave slots.
-constexpr int wgs_per_cu(bool fp8, int waves, int rg) {
-  return (147456 / shape_cfg(fp8, waves, rg).ring) < (4 * shape_cfg(fp8, waves, rg).occ / waves)
-             ? (147456 / shape_cfg(fp8, waves, rg).ring)
-             : (4 * shape_cfg(fp8, waves, rg).occ / waves);
+constexpr int wgs_per_cu(bool fp8, int waves, int rg, bool ws) {
+  return (147456 / shape_cfg(fp8, waves, rg, ws).ring) < (4 * shape_cfg(fp8, waves, rg, ws).occ / waves)
+             ? (147456 / shape_cfg(fp8, waves, rg, ws).ring)
+             : (4 * shape_cfg(fp8, waves, rg, ws).occ / waves);
 }
 
 struct SegmentLaunch {
@@ -96,6 +99,7 @@ struct SegmentShape {
   bool fp8;
   int waves;          // waves per workgroup (1, 2, 4 or 8)
   int rows_per_wave;  // 16-row groups per wave
+  bool ws;            // specialised waves: S waves and P.V waves in pairs (waves / 2 row groups)
   int chunks;         // row chunks per (request, segment)
   bool contig;        // TILE >= tile tokens: an LDS tile is one contiguous run of rows
 };

@@ -49,9 +49,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family parts.
 constexpr int kBufferFlags = 0x00020000;
-// Cache policy of the cache-row stream: non-temporal (each row is read once
-// per segment), which measured ~10% faster than the default policy.
-constexpr int kStreamPolicy = 2;
+// The cache-row stream loads are non-temporal ("nt": each row is read once per
+// piece), which measured ~10% faster than the default policy.
 // The softmax reference max moves only past this many base-2 units (p <= 2^8).
 constexpr float kLazy = 8.0f;
 
@@ -74,6 +73,40 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
 }
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Byte address in LDS of a __shared__ object (what M0 takes for LDS DMA).
+__device__ __forceinline__ unsigned lds_address(const void* shared_ptr) {
+  return (unsigned)(uintptr_t)(const LDS_AS void*)shared_ptr;
+}
+
+// Buffer resource (V#) over `bytes` bytes at `base`, no stride, raw access.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kBufferFlags;
+  return r;
+}
+
+// One 16-byte-per-lane load from a buffer straight into LDS (64 lanes fill
+// 1 KiB at lds_addr), non-temporal.  Written as inline assembly on purpose:
+// the kernels track these loads themselves with explicit vmcnt waits on the
+// ring slot they read, and the compiler, which cannot tell ring slots apart,
+// would otherwise make every LDS read and barrier wait for all of them.
+// M0 is set here for every load; kernels that use this have no other M0 user.
+__device__ __forceinline__ void dma_lds16(i32x4 rsrc, unsigned lds_addr, int voff, int soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen nt lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc),
+        "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory", "m0");
+}
 
 // LDS tile layout (32 tokens).  The 512 latent dims (also V) and the 64 rope
 // dims of a row live in two regions so that one DMA instruction (64 lanes x
@@ -193,9 +226,9 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
 // fp8 always uses 32); OCC waves per SIMD the register allocation must allow
 // (2 caps a wave at 256 registers).  Every wave of the workgroup calls it with
 // the same piece (it holds workgroup barriers).
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS>
 __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
-                                          char (*lds)[TileGeom<FP8, TT>::kTileBytes],
+                                          char (*lds)[TileGeom<FP8, TT>::kTileBytes], unsigned lds_u32,
                                           int* phys_rows, const Piece& pc) {
   using F = KvFmt<FP8>;
   static_assert(TT == 32 || (TT == 16 && !FP8), "tile shape");
@@ -207,11 +240,17 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   constexpr int kNIV = TT / kRowsPerV;                 // V-region DMA instructions
   constexpr int kNI = kTileBytes / 1024;               // all DMA instructions per tile
   constexpr int kNIw = kNIV / NW + (kNI - kNIV) / NW;   // per wave, lower bound
-  constexpr int kRowsWG = 16 * RG * NW;
+  // WS: the workgroup's waves come in pairs over one 16-row group: wave g < NG
+  // computes S = K.Q^T and the softmax of the group's rows, wave NG + g
+  // accumulates their P.V (see the specialised loop below).
+  constexpr int NG = WS ? NW / 2 : NW;                  // row groups
+  constexpr int kRowsWG = 16 * RG * NG;
+  static_assert(!WS || (RG == 1 && NW % 2 == 0), "specialised waves: pairs of one row group");
   static_assert(kTileBytes % 1024 == 0, "tile must be whole DMA instructions");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int rgw = WS ? wave % NG : wave;                             // this wave's row group
   const int g = lane >> 4;
   const int n = lane & 15;
 
@@ -237,14 +276,14 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   bool rok[RG];
 #pragma unroll
   for (int q = 0; q < RG; ++q) {
-    const int row = row0 + (wave * RG + q) * 16 + n;
+    const int row = row0 + (rgw * RG + q) * 16 + n;
     rok[q] = row < M;
     ti[q] = rok[q] ? row / H : 0;
     hh[q] = rok[q] ? row - ti[q] * H : 0;
     const int lim = rok[q] ? (p.causal ? max(0, L - qlen + ti[q] + 1) : L) : 0;
     end_row[q] = min(seg_end, lim);
   }
-  const bool wave_has_rows = row0 + wave * RG * 16 < M;
+  const bool wave_has_rows = row0 + rgw * RG * 16 < M;
 
   const float qs = p.q_scale ? *p.q_scale : 1.0f;
   const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
@@ -254,32 +293,34 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   // bf16: lane (g, n) holds row n, dims 32c + 8g .. +7 for c = 0..17.
   // fp8:  latent dims 128c + 32g .. +31 for c = 0..3 (16x16x128 MFMA) and
   //       rope dims 512 + 32c + 8g .. +7 for c = 0..1 (16x16x32 MFMA).
-  bf16x8 qop[FP8 ? 1 : RG][FP8 ? 1 : 18];
-  i32x8 qlat[FP8 ? RG : 1][4];
-  long qrope[FP8 ? RG : 1][2];
+  typedef bf16x8 QBf[FP8 ? 1 : RG][FP8 ? 1 : 18];
+  typedef i32x8 QLat[FP8 ? RG : 1][4];
+  typedef long QRope[FP8 ? RG : 1][2];
+  auto load_q = [&](QBf& qop, QLat& qlat, QRope& qrope) {
 #pragma unroll
-  for (int q = 0; q < RG; ++q) {
-    const int64_t qoff = (int64_t)(t0 + ti[q]) * p.q_stride_token + (int64_t)hh[q] * p.q_stride_head;
-    if constexpr (FP8) {
-      const uint8_t* qb = (const uint8_t*)p.q + qoff;
+    for (int q = 0; q < RG; ++q) {
+      const int64_t qoff = (int64_t)(t0 + ti[q]) * p.q_stride_token + (int64_t)hh[q] * p.q_stride_head;
+      if constexpr (FP8) {
+        const uint8_t* qb = (const uint8_t*)p.q + qoff;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 lo = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g) : u32x4{0, 0, 0, 0};
-        const u32x4 hi = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g + 16) : u32x4{0, 0, 0, 0};
-        qlat[q][c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 lo = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g) : u32x4{0, 0, 0, 0};
+          const u32x4 hi = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g + 16) : u32x4{0, 0, 0, 0};
+          qlat[q][c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
 #pragma unroll
-      for (int c = 0; c < 2; ++c) qrope[q][c] = rok[q] ? *(const long*)(qb + 512 + 32 * c + 8 * g) : 0;
-    } else {
+        for (int c = 0; c < 2; ++c) qrope[q][c] = rok[q] ? *(const long*)(qb + 512 + 32 * c + 8 * g) : 0;
+      } else {
 #pragma unroll
-      for (int c = 0; c < 18; ++c) {
-        const __bf16* qp = (const __bf16*)p.q + qoff + 32 * c + 8 * g;
-        const u32x4 v = rok[q] ? *(const u32x4*)qp : u32x4{0, 0, 0, 0};
-        qop[q][c] = __builtin_bit_cast(bf16x8, v);
+        for (int c = 0; c < 18; ++c) {
+          const __bf16* qp = (const __bf16*)p.q + qoff + 32 * c + 8 * g;
+          const u32x4 v = rok[q] ? *(const u32x4*)qp : u32x4{0, 0, 0, 0};
+          qop[q][c] = __builtin_bit_cast(bf16x8, v);
+        }
       }
     }
-  }
-  wait_vmcnt<0>();  // q is in registers before the DMA stream starts
+  };
+
 
   // ---- DMA of one 32-token tile into ring slot b ----
   // V region: instruction i of this wave fills V row index vi = wave + NW*i
@@ -314,8 +355,8 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       // Buffer descriptor over the tile's 32 rows (a guard: no offset below
       // leaves them); per instruction a scalar row offset plus one 32-bit
       // per-lane chunk offset.
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.kv + phys0 * kRowBytes), 0, TT * kRowBytes, kBufferFlags);
+      const i32x4 rsrc = make_rsrc(p.kv + phys0 * kRowBytes, TT * kRowBytes);
+      const unsigned lbase = lds_u32 + (unsigned)(b * kTileBytes);
       const int key16 = opaque(lane16);
 #pragma unroll
       for (int i = 0; i < kVPerWave; ++i) {
@@ -331,7 +372,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
           voff = (row < nvalid ? row * kRowBytes : 0) +
                  ((16 * v_cpos) ^ (32 * v_half) ^ (16 * swz_v(2 * vi)));
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(ldst + vi * 1024), 16, voff, soff, 0, kStreamPolicy);
+        dma_lds16(rsrc, lbase + vi * 1024, voff, soff);
       }
 #pragma unroll
       for (int i = 0; i < kRopePerWaveMax; ++i) {
@@ -340,7 +381,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
           const int row = ri * kRowsPerRope + rope_row_in;
           const int rr = row < nvalid ? row : 0;
           const int voff = rr * kRowBytes + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(ldst + (kNIV + ri) * 1024), 16, voff, 0, 0, kStreamPolicy);
+          dma_lds16(rsrc, lbase + (kNIV + ri) * 1024, voff, 0);
         }
       }
     } else {
@@ -384,16 +425,6 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     }
   };
 
-  // ---- running state ----
-  f32x4 acc[RG][32];
-#pragma unroll
-  for (int q = 0; q < RG; ++q)
-#pragma unroll
-    for (int d = 0; d < 32; ++d) acc[q][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[RG], m_true[RG], l_run[RG];
-#pragma unroll
-  for (int q = 0; q < RG; ++q) { m_run[q] = m_true[q] = -INFINITY; l_run[q] = 0.f; }
-
   // Per-lane LDS read geometry (see the layout note above KvFmt).
   // K reads: lane (g, t = n) reads tile row 16b + n.
   int kv_base[2], kv_x[2], kr_base[2], kr_x[2];
@@ -433,42 +464,34 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     }
   }
 
-  // ---- pipeline ----
-#pragma unroll
-  for (int k = 0; k < NBUF - 1; ++k)
-    if (k < ntiles) issue_tile(k, k);
+  // ---- per-tile steps ----
+  // LDS operands are prefetched several MFMA steps ahead: one MFMA issues every
+  // 16-32 cycles, while an LDS read takes ~100-200 cycles to return.  (Kernels
+  // sized for two waves per SIMD have half the registers: shallower there.)
+  // (bf16 with two waves per SIMD: two steps ahead, which keeps the Q, S and
+  // accumulator registers clear of spills.)
+  constexpr int kPF = OCC == 2 ? (FP8 ? 4 : 2) : 8;
+  constexpr int kPFL = OCC == 2 ? 2 : 4;
+  constexpr int kPFV = OCC == 2 ? (FP8 ? 4 : 2) : 8;
+  typedef typename std::conditional<kNB == 2, bf16x8, i16x4>::type POp;
+  typedef typename std::conditional<FP8, i32x2, POp>::type VRaw;
+  typedef f32x4 Acc[RG][32];
+  typedef f32x4 SBlk[RG][2];
+  // P^T operand of one row group (the layout of the S^T accumulator, so it
+  // needs no data movement): bf16 values, or e4m3 codes packed in a long.
+  struct PVal {
+    POp pb[RG];
+    long pb8[FP8 ? RG : 1];
+  };
 
-  for (int k = 0; k < ntiles; ++k) {
-    if constexpr (NBUF == 1) {
-      // Single slot: load, wait, compute; other waves on the SIMD overlap.
-      if (k > 0) __syncthreads();  // every wave is done with the slot
-      issue_tile(k, 0);
-      wait_vmcnt<0>();
-      __syncthreads();
-    } else {
-      wait_tiles<kNIw, (NBUF >= 2 ? NBUF - 2 : 0)>(min(NBUF - 2, ntiles - 1 - k));
-      __syncthreads();
-      if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
-    }
-    if (!wave_has_rows) continue;
-
-    const char* buf = lds[k % NBUF];
-    const int tile_start = seg_start + k * TT;
-    int kvb[2], kvx[2], krb[2], krx[2], vtb[2], vtx[2];
+  // S^T = K . Q^T for the tile's 16-token blocks.
+  auto qk_tile = [&](const char* buf, const QBf& qop, const QLat& qlat, const QRope& qrope, SBlk& sblk) {
+    int kvb[2], kvx[2], krb[2], krx[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       kvb[b] = opaque(kv_base[b]); kvx[b] = opaque(kv_x[b]);
       krb[b] = opaque(kr_base[b]); krx[b] = opaque(kr_x[b]);
-      vtb[b] = opaque(vt_base[b]); vtx[b] = opaque(vt_x[b]);
     }
-
-    // S^T = K . Q^T for the tile's 16-token blocks.  LDS operands are
-    // prefetched several MFMA steps ahead: one MFMA issues every 16-32
-    // cycles, while an LDS read takes ~100-200 cycles to return.
-    // (8-wave workgroups run two waves per SIMD, which hide part of the
-    // latency for each other, and have half the registers: shallower there.)
-    constexpr int kPF = OCC == 2 ? 4 : 8;
-    f32x4 sblk[RG][2];
 #pragma unroll
     for (int q = 0; q < RG; ++q) sblk[q][0] = sblk[q][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (FP8) {
@@ -480,7 +503,6 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       constexpr int kLat = 4 * kNB;
-      constexpr int kPFL = OCC == 2 ? 2 : 4;
       i32x8 kl[kPFL];
 #pragma unroll
       for (int i = 0; i < kPFL; ++i) kl[i] = lat_load(i);
@@ -528,15 +550,15 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
 
-    // Base-2 online softmax per row over this tile.  The reference max m_run
-    // only moves when the tile max exceeds it by more than kLazy (so p <= 2^kLazy);
-    // m_true tracks the exact max and the end rescales to it once.
-    typedef typename std::conditional<kNB == 2, bf16x8, i16x4>::type POp;
-    POp pb[RG];
-    long pb8[FP8 ? RG : 1];
+  // Base-2 online softmax per row over one tile.  The reference max m_run
+  // only moves when the tile max exceeds it by more than kLazy (so p <= 2^kLazy);
+  // m_true tracks the exact max and the end rescales to it once.  Returns
+  // whether this lane's rows need the accumulator rescaled by alpha.
+  auto softmax_tile = [&](const SBlk& sblk, int tile_start, float (&m_run)[RG], float (&m_true)[RG],
+                          float (&l_run)[RG], PVal& pv_out, float (&alpha)[RG]) -> bool {
     bool rescale = false;
-    float alpha[RG];
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
       float x[4 * kNB];
@@ -575,29 +597,34 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w0, true);
         int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4], pv[5], 0, false);
         w1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[6], pv[7], w1, true);
-        pb8[q] = (long)(unsigned)w0 | ((long)(unsigned)w1 << 32);
+        pv_out.pb8[q] = (long)(unsigned)w0 | ((long)(unsigned)w1 << 32);
       } else if constexpr (kNB == 2) {
-        pb[q] = to_bf16x8(pv);
+        pv_out.pb[q] = to_bf16x8(pv);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pb[q][i] = __builtin_bit_cast(short, (__bf16)pv[i]);
+        for (int i = 0; i < 4; ++i) pv_out.pb[q][i] = __builtin_bit_cast(short, (__bf16)pv[i]);
       }
     }
-    if (__ballot(rescale)) {
-      // one accumulator group at a time: keeps the AGPR -> VGPR -> AGPR
-      // round trip to four registers
-#pragma unroll
-      for (int q = 0; q < RG; ++q)
-#pragma unroll
-        for (int d = 0; d < 32; ++d) {
-          acc[q][d] *= alpha[q];
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    return rescale;
+  };
 
-    // O^T += V^T . P^T over 32 dim blocks of 16, operands prefetched kPFV ahead.
-    typedef typename std::conditional<FP8, i32x2, typename std::conditional<kNB == 2, bf16x8, i16x4>::type>::type VRaw;
+  // acc *= alpha, one accumulator group at a time: keeps the AGPR -> VGPR ->
+  // AGPR round trip to four registers.
+  auto rescale_acc = [&](Acc& acc, const float (&alpha)[RG]) {
+#pragma unroll
+    for (int q = 0; q < RG; ++q)
+#pragma unroll
+      for (int d = 0; d < 32; ++d) {
+        acc[q][d] *= alpha[q];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
+  // O^T += V^T . P^T over 32 dim blocks of 16, operands prefetched kPFV ahead.
+  auto pv_tile = [&](const char* buf, Acc& acc, const PVal& pvv) {
+    int vtb[2], vtx[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) { vtb[b] = opaque(vt_base[b]); vtx[b] = opaque(vt_x[b]); }
     auto v_load = [&](int db) -> VRaw {
       if constexpr (kNB == 1) {
         // one 16-token block: k-slots 4g..4g+3 from a single transpose read
@@ -616,7 +643,6 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
-    constexpr int kPFV = OCC == 2 ? 4 : 8;
     VRaw vop[kPFV];
 #pragma unroll
     for (int i = 0; i < kPFV; ++i) vop[i] = v_load(i);
@@ -627,101 +653,255 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       if constexpr (kNB == 1) {
 #pragma unroll
         for (int q = 0; q < RG; ++q)
-          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur, pb[q], acc[q][db], 0, 0, 0);
+          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur, pvv.pb[q], acc[q][db], 0, 0, 0);
       } else if constexpr (FP8) {
         const long va = __builtin_bit_cast(long, cur);
 #pragma unroll
         for (int q = 0; q < RG; ++q)
-          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va, pb8[q], acc[q][db], 0, 0, 0);
+          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va, pvv.pb8[q], acc[q][db], 0, 0, 0);
       } else {
 #pragma unroll
         for (int q = 0; q < RG; ++q)
-          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pb[q], acc[q][db], 0, 0, 0);
+          acc[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pvv.pb[q], acc[q][db], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
 
-  // Final exact-max correction of the lazily rescaled state.
+  // ---- the piece's result ----
+  // acc holds sum_j 2^(x_j - m_true) V_j in code units for each row, l_tot
+  // the matching sum of weights (already reduced over the lanes of a row).
+  auto write_result = [&](const Acc& acc, const float (&l_tot_in)[RG], const float (&m_fin)[RG], bool bad_all) {
 #pragma unroll
-  for (int q = 0; q < RG; ++q) {
-    const float f = (m_true[q] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[q] - m_true[q]);
-    l_run[q] *= f;
-#pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      acc[q][d] *= f;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // ---- write the piece's result ----
-  bad = __syncthreads_or(bad ? 1 : 0) != 0;
-#pragma unroll
-  for (int q = 0; q < RG; ++q) {
-    float l_tot = l_run[q] + __shfl_xor(l_run[q], 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (!rok[q]) continue;
-    // One store loop for every destination: values acc * mult, as fp32 or
-    // as 16-bit (bf16 rounded to nearest even, or fp16).
-    float mult, stat0, stat1;
-    float* stat0_p;
-    float* stat1_p;
-    char* dst;
-    int kind;  // 0 bf16, 1 fp16, 2 fp32
-    if (pc.mode == kOutFinal) {
-      // Normalised output and natural-log LSE; an optional sink joins the
-      // softmax as one more logit with a zero value.
-      const bool has = m_true[q] > -INFINITY;
-      float lse = has ? kLn2 * (m_true[q] + __log2f(l_tot)) : -INFINITY;
-      mult = has ? ks / l_tot : 0.f;
-      if (p.sinks) {
-        const float nl = logaddexp_f(lse, p.sinks[hh[q]]);
-        mult = has ? mult * expf(lse - nl) : 0.f;
-        lse = nl;
-      }
-      if (bad) { lse = __builtin_nanf(""); mult = __builtin_nanf(""); }
-      const int64_t orow = (int64_t)(t0 + ti[q]) * H + hh[q];
-      kind = p.out_dtype;
-      dst = (char*)p.out + (orow * kKvRank + 4 * g) * (kind == 2 ? 4 : 2);
-      stat0 = lse;
-      stat0_p = p.lse + orow;
-      stat1 = 0.f;
-      stat1_p = nullptr;
-    } else {
-      const int64_t slot = pc.mode == kOutSegment
-                               ? ((int64_t)(t0 + ti[q]) * H + hh[q]) * p.num_segments + pc.s
-                               : pc.prow0 + (wave * RG + q) * 16 + n;
-      mult = ks;
-      kind = 2;
-      dst = (char*)(p.seg_out + slot * kKvRank + 4 * g);
-      stat0 = bad ? __builtin_nanf("") : m_true[q];
-      stat0_p = p.seg_max + slot;
-      stat1 = l_tot;
-      stat1_p = p.seg_sum + slot;
-    }
-#pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const f32x4 o = acc[q][db] * mult;
-      if (kind == 2) {
-        *(f32x4*)(dst + 64 * db) = o;
-      } else {
-        u32x2 v;
-        if (kind == 0) {
-          v[0] = (unsigned)f32_to_bf16_rne(o[0]) | ((unsigned)f32_to_bf16_rne(o[1]) << 16);
-          v[1] = (unsigned)f32_to_bf16_rne(o[2]) | ((unsigned)f32_to_bf16_rne(o[3]) << 16);
-        } else {
-          v[0] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[0]) |
-                 ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[1]) << 16);
-          v[1] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[2]) |
-                 ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[3]) << 16);
+    for (int q = 0; q < RG; ++q) {
+      const float l_tot = l_tot_in[q];
+      if (!rok[q]) continue;
+      // One store loop for every destination: values acc * mult, as fp32 or
+      // as 16-bit (bf16 rounded to nearest even, or fp16).
+      float mult, stat0, stat1;
+      float* stat0_p;
+      float* stat1_p;
+      char* dst;
+      int kind;  // 0 bf16, 1 fp16, 2 fp32
+      if (pc.mode == kOutFinal) {
+        // Normalised output and natural-log LSE; an optional sink joins the
+        // softmax as one more logit with a zero value.
+        const bool has = m_fin[q] > -INFINITY;
+        float lse = has ? kLn2 * (m_fin[q] + __log2f(l_tot)) : -INFINITY;
+        mult = has ? ks / l_tot : 0.f;
+        if (p.sinks) {
+          const float nl = logaddexp_f(lse, p.sinks[hh[q]]);
+          mult = has ? mult * expf(lse - nl) : 0.f;
+          lse = nl;
         }
-        *(u32x2*)(dst + 32 * db) = v;
+        if (bad_all) { lse = __builtin_nanf(""); mult = __builtin_nanf(""); }
+        const int64_t orow = (int64_t)(t0 + ti[q]) * H + hh[q];
+        kind = p.out_dtype;
+        dst = (char*)p.out + (orow * kKvRank + 4 * g) * (kind == 2 ? 4 : 2);
+        stat0 = lse;
+        stat0_p = p.lse + orow;
+        stat1 = 0.f;
+        stat1_p = nullptr;
+      } else {
+        const int64_t slot = pc.mode == kOutSegment
+                                 ? ((int64_t)(t0 + ti[q]) * H + hh[q]) * p.num_segments + pc.s
+                                 : pc.prow0 + (rgw * RG + q) * 16 + n;
+        mult = ks;
+        kind = 2;
+        dst = (char*)(p.seg_out + slot * kKvRank + 4 * g);
+        stat0 = bad_all ? __builtin_nanf("") : m_fin[q];
+        stat0_p = p.seg_max + slot;
+        stat1 = l_tot;
+        stat1_p = p.seg_sum + slot;
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < 32; ++db) {
+        const f32x4 o = acc[q][db] * mult;
+        if (kind == 2) {
+          *(f32x4*)(dst + 64 * db) = o;
+        } else {
+          u32x2 v;
+          if (kind == 0) {
+            v[0] = (unsigned)f32_to_bf16_rne(o[0]) | ((unsigned)f32_to_bf16_rne(o[1]) << 16);
+            v[1] = (unsigned)f32_to_bf16_rne(o[2]) | ((unsigned)f32_to_bf16_rne(o[3]) << 16);
+          } else {
+            v[0] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[0]) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[1]) << 16);
+            v[1] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[2]) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[3]) << 16);
+          }
+          *(u32x2*)(dst + 32 * db) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (g == 0) {
+        *stat0_p = stat0;
+        if (stat1_p) *stat1_p = stat1;
+      }
     }
-    if (g == 0) {
-      *stat0_p = stat0;
-      if (stat1_p) *stat1_p = stat1;
+  };
+
+  if constexpr (!WS) {
+    // ---- every wave: QK, softmax and P.V of its own rows, tile after tile ----
+    QBf qop;
+    QLat qlat;
+    QRope qrope;
+    load_q(qop, qlat, qrope);
+    wait_vmcnt<0>();  // q is in registers before the DMA stream starts
+    Acc acc;
+#pragma unroll
+    for (int q = 0; q < RG; ++q)
+#pragma unroll
+      for (int d = 0; d < 32; ++d) acc[q][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[RG], m_true[RG], l_run[RG];
+#pragma unroll
+    for (int q = 0; q < RG; ++q) { m_run[q] = m_true[q] = -INFINITY; l_run[q] = 0.f; }
+
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (k < ntiles) issue_tile(k, k);
+
+    for (int k = 0; k < ntiles; ++k) {
+      if constexpr (NBUF == 1) {
+        // Single slot: load, wait, compute; other waves on the SIMD overlap.
+        if (k > 0) __syncthreads();  // every wave is done with the slot
+        issue_tile(k, 0);
+        wait_vmcnt<0>();
+        __syncthreads();
+      } else if constexpr (NW == 1) {
+        // A lone wave owns its ring: the slot of tile k-1 is free as soon as
+        // its reads returned, so the next tile is issued before waiting for
+        // tile k and NBUF tiles are in flight during the wait.
+        if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+        wait_tiles<kNIw, NBUF - 1>(min(NBUF - 1, ntiles - 1 - k));
+      } else {
+        wait_tiles<kNIw, (NBUF >= 2 ? NBUF - 2 : 0)>(min(NBUF - 2, ntiles - 1 - k));
+        __syncthreads();
+        if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+      }
+      if (!wave_has_rows) continue;
+      const char* buf = lds[k % NBUF];
+      SBlk sblk;
+      qk_tile(buf, qop, qlat, qrope, sblk);
+      PVal pvv;
+      float alpha[RG];
+      const bool resc = softmax_tile(sblk, seg_start + k * TT, m_run, m_true, l_run, pvv, alpha);
+      if (__ballot(resc)) rescale_acc(acc, alpha);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_tile(buf, acc, pvv);
+    }
+
+    // Final exact-max correction of the lazily rescaled state.
+    float l_tot[RG];
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      const float f = (m_true[q] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[q] - m_true[q]);
+      l_run[q] *= f;
+#pragma unroll
+      for (int d = 0; d < 32; ++d) {
+        acc[q][d] *= f;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_tot[q] = l_run[q] + __shfl_xor(l_run[q], 16);
+      l_tot[q] += __shfl_xor(l_tot[q], 32);
+    }
+    bad = __syncthreads_or(bad ? 1 : 0) != 0;
+    write_result(acc, l_tot, m_true, bad);
+  } else {
+    // ---- specialised waves ----
+    // Iteration k (k = -1 .. ntiles-1): the S wave of a row group computes
+    // S = K.Q^T and the softmax of tile k+1 and leaves P^T (8 bytes a lane)
+    // and the rescale factors in LDS slot (k+1) % 2; its partner P.V wave
+    // takes P^T of tile k from slot k % 2, rescales its accumulator and
+    // accumulates V^T.P^T of tile k.  One barrier per iteration orders both,
+    // and every wave runs the same barrier sequence.  Tile j sits in ring slot
+    // j % NBUF; iteration k refills the slot of tile k - 1 (done with), so
+    // tiles k+2 .. k+NBUF-2 stay in flight while k and k+1 are in use.
+    static_assert(FP8 ? (kNB == 2) : (kNB == 1), "specialised waves: 8-byte P^T operands");
+    __shared__ long ws_p[2][NG][64];
+    __shared__ float ws_alpha[2][NG][16];
+    __shared__ int ws_flag[2][NG];
+    __shared__ float ws_fin[NG][3][16];
+    const bool s_wave = wave < NG;
+
+#pragma unroll
+    for (int k = 0; k < NBUF - 2; ++k)
+      if (k < ntiles) issue_tile(k, k);
+
+    if (s_wave) {
+      QBf qop;
+      QLat qlat;
+      QRope qrope;
+      load_q(qop, qlat, qrope);
+      float m_run[RG], m_true[RG], l_run[RG];
+      m_run[0] = m_true[0] = -INFINITY;
+      l_run[0] = 0.f;
+      for (int k = -1; k < ntiles; ++k) {
+        if (k + 1 < ntiles) wait_tiles<kNIw, (NBUF >= 3 ? NBUF - 3 : 0)>(min(NBUF - 3, ntiles - 2 - k));
+        __syncthreads();
+        if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+        if (k + 1 < ntiles && wave_has_rows) {
+          const int ps = (k + 1) & 1;
+          SBlk sblk;
+          qk_tile(lds[(k + 1) % NBUF], qop, qlat, qrope, sblk);
+          PVal pvv;
+          float alpha[RG];
+          const bool resc = softmax_tile(sblk, seg_start + (k + 1) * TT, m_run, m_true, l_run, pvv, alpha);
+          const bool any = __ballot(resc) != 0;
+          long word;
+          if constexpr (FP8) word = pvv.pb8[0];
+          else word = __builtin_bit_cast(long, pvv.pb[0]);
+          ws_p[ps][rgw][lane] = word;
+          if (g == 0) ws_alpha[ps][rgw][n] = alpha[0];
+          if (lane == 0) ws_flag[ps][rgw] = any ? 1 : 0;
+        }
+      }
+      // Final exact-max correction factor and the row sums, for the P.V wave.
+      const float f = (m_true[0] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[0] - m_true[0]);
+      float l_tot = l_run[0] + __shfl_xor(l_run[0], 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      if (g == 0) {
+        ws_fin[rgw][0][n] = f;
+        ws_fin[rgw][1][n] = l_tot * f;
+        ws_fin[rgw][2][n] = m_true[0];
+      }
+      __syncthreads();
+      bad = __syncthreads_or(bad ? 1 : 0) != 0;
+    } else {
+      Acc acc;
+#pragma unroll
+      for (int d = 0; d < 32; ++d) acc[0][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = -1; k < ntiles; ++k) {
+        if (k + 1 < ntiles) wait_tiles<kNIw, (NBUF >= 3 ? NBUF - 3 : 0)>(min(NBUF - 3, ntiles - 2 - k));
+        __syncthreads();
+        if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+        if (k >= 0 && wave_has_rows) {
+          const int ps = k & 1;
+          PVal pvv;
+          const long word = ws_p[ps][rgw][lane];
+          if constexpr (FP8) pvv.pb8[0] = word;
+          else pvv.pb[0] = __builtin_bit_cast(POp, word);
+          if (ws_flag[ps][rgw]) {
+            float alpha[RG];
+            alpha[0] = ws_alpha[ps][rgw][n];
+            rescale_acc(acc, alpha);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          pv_tile(lds[k % NBUF], acc, pvv);
+        }
+      }
+      __syncthreads();
+      const float f = ws_fin[rgw][0][n];
+      float l_tot[RG], m_fin[RG];
+      l_tot[0] = ws_fin[rgw][1][n];
+      m_fin[0] = ws_fin[rgw][2][n];
+#pragma unroll
+      for (int d = 0; d < 32; ++d) {
+        acc[0][d] *= f;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bad = __syncthreads_or(bad ? 1 : 0) != 0;
+      write_result(acc, l_tot, m_fin, bad);
     }
   }
 }
@@ -729,12 +909,12 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
 // Segment kernel: one workgroup per (segment, request, row chunk); the key
 // partition is the segment formula of the merge page's module description
 // (span = cdiv(len, S * TILE) * TILE; segment s = [s * span, min((s+1) * span, len))).
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void segment_kernel(
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][TileGeom<FP8, TT>::kTileBytes];
   __shared__ int phys_rows[CONTIG ? 1 : TT];
-  constexpr int kRowsWG = 16 * RG * NW;
+  constexpr int kRowsWG = 16 * RG * (WS ? NW / 2 : NW);
   const int s = blockIdx.x;
   const int r = blockIdx.y;
   const int chunk = blockIdx.z;
@@ -755,7 +935,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
   pc.r = r; pc.t0 = t0; pc.qlen = qlen; pc.L = L; pc.row0 = row0;
   pc.seg_start = seg_start; pc.seg_end = min(seg_start + span, L);
   pc.mode = kOutSegment; pc.s = s; pc.prow0 = 0;
-  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC>(p, lds, phys_rows, pc);
+  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
 }
 
 // Work units of request r for a workgroup shape of rows_wg rows and TT-token
@@ -794,12 +974,12 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // boundary leaves base-2 partials in the workgroup's slot 0 (its first piece)
 // or slot 1 (its last piece) for the merge.  Workgroup 0 also stores the
 // per-request unit offsets the merge uses to find the pieces.
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void split_kernel(
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][TileGeom<FP8, TT>::kTileBytes];
   __shared__ int phys_rows[CONTIG ? 1 : TT];
-  constexpr int kRowsWG = 16 * RG * NW;
+  constexpr int kRowsWG = 16 * RG * (WS ? NW / 2 : NW);
   const int lane = threadIdx.x & 63;
   const int R = p.num_reqs;
   const int G = gridDim.x;
@@ -866,7 +1046,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
     pc.mode = (a == 0 && b == nt) ? kOutFinal : kOutSplit;
     pc.s = 0;
     pc.prow0 = ((int64_t)gw * 2 + (pos == s_g ? 0 : 1)) * kRowsWG;
-    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC>(p, lds, phys_rows, pc);
+    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
     pos += b - a;
   }
 }
@@ -1095,43 +1275,40 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
   if (lane == 0) p.lse[row] = lse;
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG>
+template <bool FP8, int NW, int RG, bool CONTIG, bool WS>
 hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
-  // LDS ring per workgroup: 36 KiB with 1 wave (four workgroups per CU; bf16
-  // uses 16-token tiles there), 72 KiB with 2 waves (two per CU), 144 KiB
-  // with 4 waves (one per CU).
-  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG);
+  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG, WS);
   constexpr int kTT = kCfg.tt;
   constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
   constexpr int kRing = kCfg.ring / kTileBytes;
   dim3 grid(a.num_segments, a.num_reqs, chunks);
-  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ>), grid, dim3(64 * NW), 0,
+  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS>), grid, dim3(64 * NW), 0,
                      stream, a);
   return hipGetLastError();
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG>
+template <bool FP8, int NW, int RG, bool CONTIG, bool WS>
 hipError_t launch_split(const SegmentLaunch& a, int grid_wgs, hipStream_t stream) {
-  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG);
+  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG, WS);
   constexpr int kTT = kCfg.tt;
   constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
   constexpr int kRing = kCfg.ring / kTileBytes;
-  hipLaunchKernelGGL((split_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ>), dim3(grid_wgs), dim3(64 * NW), 0,
-                     stream, a);
+  hipLaunchKernelGGL((split_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS>), dim3(grid_wgs), dim3(64 * NW),
+                     0, stream, a);
   return hipGetLastError();
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG>
+template <bool FP8, int NW, int RG, bool CONTIG, bool WS = false>
 hipError_t launch_any(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
-  return split_wgs > 0 ? launch_split<FP8, NW, RG, CONTIG>(a, split_wgs, stream)
-                       : launch_seg<FP8, NW, RG, CONTIG>(a, sh.chunks, stream);
+  return split_wgs > 0 ? launch_split<FP8, NW, RG, CONTIG, WS>(a, split_wgs, stream)
+                       : launch_seg<FP8, NW, RG, CONTIG, WS>(a, sh.chunks, stream);
 }
 
 template <bool FP8, bool CONTIG>
 hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
-  if (sh.rows_per_wave == 2) {
-    return sh.waves == 2 ? launch_any<FP8, 2, 2, CONTIG>(a, sh, split_wgs, stream)
-                         : launch_any<FP8, 4, 2, CONTIG>(a, sh, split_wgs, stream);
+  if (sh.ws) {
+    return sh.waves == 4 ? launch_any<FP8, 4, 1, CONTIG, true>(a, sh, split_wgs, stream)
+                         : launch_any<FP8, 8, 1, CONTIG, true>(a, sh, split_wgs, stream);
   }
   switch (sh.waves) {
     case 1: return launch_any<FP8, 1, 1, CONTIG>(a, sh, split_wgs, stream);
@@ -1146,15 +1323,17 @@ hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, int 
 SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
   SegmentShape sh;
   sh.fp8 = fp8;
+  sh.ws = false;
+  sh.rows_per_wave = 1;
   const int groups = (max_qlen * num_heads + 15) / 16;
-  // groups of 16 rows -> (waves, row groups per wave)
-  if (groups <= 1)      { sh.waves = 1; sh.rows_per_wave = 1; }
-  else if (groups == 2) { sh.waves = 2; sh.rows_per_wave = 1; }
-  else if (groups <= 4) { sh.waves = 4; sh.rows_per_wave = 1; }
-  else                  { sh.waves = 8; sh.rows_per_wave = 1; }
-  const int per_wg = sh.waves * sh.rows_per_wave;
-  sh.chunks = (groups + per_wg - 1) / per_wg;
-  sh.contig = tile >= tile_tokens(fp8, sh.waves, sh.rows_per_wave);
+  // groups of 16 rows -> waves per workgroup
+  if (groups <= 1)      { sh.waves = 1; }
+  else if (groups == 2) { sh.waves = 2; }
+  else if (groups <= 4) { sh.waves = 4; }
+  else                  { sh.waves = 8; }
+  const int rows_wg = 16 * sh.rows_per_wave * (sh.ws ? sh.waves / 2 : sh.waves);
+  sh.chunks = (max_qlen * num_heads + rows_wg - 1) / rows_wg;
+  sh.contig = tile >= tile_tokens(fp8, sh.waves, sh.rows_per_wave, sh.ws);
   return sh;
 }
 
