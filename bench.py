@@ -248,8 +248,8 @@ def profiled_traffic(workload):
                     k, _, v = line.partition(":")
                     kv[k.strip()] = v.strip()
         if (kv.get("workload") == workload and kv.get("kernel_source_sha256_16") == digest
-                and "segment_kernel_traffic_bytes" in kv):
-            return int(kv["segment_kernel_traffic_bytes"])
+                and "stream_kernel_traffic_bytes" in kv):
+            return int(kv["stream_kernel_traffic_bytes"])
     return None
 
 

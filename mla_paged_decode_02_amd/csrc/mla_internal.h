@@ -12,8 +12,8 @@ constexpr int kHeadDim = 576;
 constexpr int kKvRank = 512;
 // Launch shape of the segment kernel per (dtype, waves per workgroup, 16-row
 // groups per wave):
-//  tt   tokens per LDS tile (16 for bf16 with one or four waves: 18 KiB
-//       tiles, so a ring holds enough of them in flight; else 32),
+//  tt   tokens per LDS tile (bf16 16 except with two waves: 18 KiB tiles,
+//       so a ring holds enough of them in flight; fp8 32),
 //  ring LDS ring bytes per workgroup,
 //  occ  waves per SIMD the kernel's registers are sized for (2 caps a wave
 //       at 256 registers; 1 allows 512, which two row groups need).
@@ -35,7 +35,7 @@ constexpr ShapeCfg shape_cfg(bool fp8, int waves, int rg, bool ws) {
        : waves == 1 ? ShapeCfg{fp8 ? 32 : 16, 36864, 1}
        : waves == 2 ? ShapeCfg{32, 73728, 1}
        : waves == 4 ? ShapeCfg{fp8 ? 32 : 16, 73728, 2}
-                    : ShapeCfg{32, 147456, 2};
+                    : ShapeCfg{fp8 ? 32 : 16, 147456, 2};
 }
 constexpr int tile_tokens(bool fp8, int waves, int rg, bool ws) { return shape_cfg(fp8, waves, rg, ws).tt; }
 // Workgroups one CU holds at once: bound by LDS and by wave slots.
