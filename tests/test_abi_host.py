@@ -150,3 +150,59 @@ def test_dtype_pair_mismatch_raises():
     with pytest.raises(ValueError, match="must match"):
         m.make_problem(q, kv, torch.zeros((1, 1), dtype=torch.int32), torch.ones(1, dtype=torch.int32),
                        softmax_scale=0.1, max_seq_len=1)
+
+
+# ------------------------------------------------------ balanced split plan --
+
+def _split_problem(H=16, R=4, L=1000, block=16, dtype=torch.bfloat16, qlen=1, **kw):
+    T = R * qlen
+    q = torch.zeros((T, H, 576), dtype=dtype)
+    kv = torch.zeros((R * ((L + block - 1) // block), block, 576), dtype=dtype)
+    bt = torch.zeros((R, (L + block - 1) // block), dtype=torch.int32)
+    sl = torch.full((R,), L, dtype=torch.int32)
+    qo = torch.arange(0, T + 1, qlen, dtype=torch.int32) if qlen > 1 else None
+    p = m.make_problem(q, kv, bt, sl, softmax_scale=0.1, max_seq_len=L, qo_indptr=qo,
+                       max_qlen=qlen if qlen > 1 else None, sum_seq_lens=R * L, **kw)
+    return p
+
+
+def test_split_plan_shapes():
+    # one 16-row group: one wave per workgroup, 16-token units (bf16) / 32 (fp8)
+    g, rows, tt = m.split_plan(_split_problem(H=16))
+    assert (rows, tt) == (16, 16) and 1 <= g <= 1024
+    assert m.split_plan(_split_problem(H=16, dtype=torch.float8_e4m3fn))[1:] == (16, 32)
+    # 64 heads: four waves of 16 rows; 128 heads: eight
+    assert m.split_plan(_split_problem(H=64, dtype=torch.float8_e4m3fn))[1:] == (64, 32)
+    assert m.split_plan(_split_problem(H=128, block=256))[1:] == (128, 16)
+    # never more workgroups than units: 4 requests x cdiv(1000, 16) tiles
+    assert m.split_plan(_split_problem(H=16))[0] <= 4 * (63 + 1)
+
+
+def test_split_plan_respects_max_workgroups_and_segment_mode():
+    assert m.split_plan(_split_problem(max_workgroups=3))[0] == 3
+    assert m.split_plan(_split_problem(max_workgroups=1))[0] == 1
+    # a fixed segment count uses the segment partition, not the split
+    assert m.split_plan(_split_problem(num_segments=4)) is None
+    with pytest.raises(m.MlaError, match="max_workgroups"):
+        m.split_plan(_split_problem(max_workgroups=-1))
+
+
+def test_split_workspace_covers_two_slots_per_workgroup():
+    p = _split_problem(H=32, R=5, max_workgroups=7)
+    g, rows, tt = m.split_plan(p)
+    assert (g, rows) == (7, 32)
+    need = m.workspace_bytes(p)
+    part_rows = g * 2 * rows
+    assert need >= part_rows * 512 * 4 + 2 * part_rows * 4 + (5 + 1) * 4
+    # the segment partition of the same batch needs [T, H, S, 512] instead
+    p.num_segments = 3
+    assert m.workspace_bytes(p) >= 5 * 32 * 3 * 512 * 4
+
+
+def test_decode_stage_rejects_bad_stage_before_launch():
+    L = m.lib()
+    p = _split_problem()
+    assert L.mla_decode_stage(ctypes.byref(p), None, 16, 1, 16, None, 0, 3, None) == m.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_stage(ctypes.byref(p), None, 16, 1, 16, None, 0, 0, None) == m.MLA_ERR_INVALID_ARG
+    # a valid stage with no workspace fails on the workspace, still before any launch
+    assert L.mla_decode_stage(ctypes.byref(p), None, 16, 1, 16, None, 0, 1, None) == m.MLA_ERR_WORKSPACE
