@@ -181,7 +181,9 @@ SplitPlan plan_split(const mla_problem* p, int tile) {
   // Units the batch holds at most (exact up to one tile per request when the
   // caller gives the summed lengths).
   const int64_t est = p->sum_seq_lens > 0 ? chunks * (cdiv64(p->sum_seq_lens, sp.tt) + p->num_reqs) : max_units;
-  const int64_t slots = (int64_t)device_cus() * mla::wgs_per_cu(sp.sh.fp8, sp.sh.waves, sp.sh.rows_per_wave, sp.sh.ws);
+  // (k-split waves: one workgroup holds ks waves' rings)
+  const int64_t slots =
+      (int64_t)device_cus() * mla::wgs_per_cu(sp.sh.fp8, sp.sh.waves, sp.sh.rows_per_wave, sp.sh.ws) / sp.sh.ks;
   int64_t G = slots < est ? slots : est;
   if (p->max_workgroups > 0 && G > p->max_workgroups) G = p->max_workgroups;
   if (G < 1) G = 1;

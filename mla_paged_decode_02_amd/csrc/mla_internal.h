@@ -102,7 +102,16 @@ struct SegmentShape {
   bool ws;            // specialised waves: S waves and P.V waves in pairs (waves / 2 row groups)
   int chunks;         // row chunks per (request, segment)
   bool contig;        // TILE >= tile tokens: an LDS tile is one contiguous run of rows
+  int ks;             // balanced split: k-split waves per workgroup (1 = none)
 };
+
+// Balanced split with one 16-row group: four waves per workgroup share every
+// piece tile by tile and combine at its end, one workgroup per CU (the same
+// four waves per CU as four one-wave workgroups, a quarter of the pieces).
+constexpr int kSplitKs = 4;
+constexpr int split_ks(int waves, int rg, bool ws, bool contig) {
+  return (waves == 1 && rg == 1 && !ws && contig) ? kSplitKs : 1;
+}
 
 SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile);
 

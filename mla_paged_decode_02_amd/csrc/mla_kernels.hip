@@ -195,6 +195,7 @@ struct Piece {
   int mode;        // kOutSegment, kOutFinal or kOutSplit
   int s;           // segment index (kOutSegment)
   int64_t prow0;   // first partial row of the piece (kOutSplit)
+  int phase;       // k-split waves: the wave that takes the piece's first tile
 };
 // Where a piece's result goes:
 //  segment: base-2 partials of segment s at [t, h, s] of the segment buffers;
@@ -226,7 +227,7 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
 // fp8 always uses 32); OCC waves per SIMD the register allocation must allow
 // (2 caps a wave at 256 registers).  Every wave of the workgroup calls it with
 // the same piece (it holds workgroup barriers).
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, int KS = 1>
 __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
                                           char (*lds)[TileGeom<FP8, TT>::kTileBytes], unsigned lds_u32,
                                           int* phys_rows, const Piece& pc) {
@@ -249,7 +250,9 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   static_assert(kTileBytes % 1024 == 0, "tile must be whole DMA instructions");
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  // k-split waves (KS > 1) all take the one row group: their wave index
+  // (kw below) picks tiles, not rows.
+  const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int rgw = WS ? wave % NG : wave;                             // this wave's row group
   const int g = lane >> 4;
   const int n = lane & 15;
@@ -671,7 +674,11 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   // ---- the piece's result ----
   // acc holds sum_j 2^(x_j - m_true) V_j in code units for each row, l_tot
   // the matching sum of weights (already reduced over the lanes of a row).
-  auto write_result = [&](const Acc& acc, const float (&l_tot_in)[RG], const float (&m_fin)[RG], bool bad_all) {
+  // The dim blocks db0 .. db0 + ND - 1 of every row are stored (ND = 32 unless
+  // k-split waves share the store); the row statistics only if with_stats.
+  auto write_result = [&](const auto& acc, const float (&l_tot_in)[RG], const float (&m_fin)[RG], bool bad_all,
+                          int db0, bool with_stats) {
+    constexpr int ND = sizeof(acc[0]) / sizeof(f32x4);
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
       const float l_tot = l_tot_in[q];
@@ -697,7 +704,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         if (bad_all) { lse = __builtin_nanf(""); mult = __builtin_nanf(""); }
         const int64_t orow = (int64_t)(t0 + ti[q]) * H + hh[q];
         kind = p.out_dtype;
-        dst = (char*)p.out + (orow * kKvRank + 4 * g) * (kind == 2 ? 4 : 2);
+        dst = (char*)p.out + (orow * kKvRank + 16 * db0 + 4 * g) * (kind == 2 ? 4 : 2);
         stat0 = lse;
         stat0_p = p.lse + orow;
         stat1 = 0.f;
@@ -708,14 +715,14 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
                                  : pc.prow0 + (rgw * RG + q) * 16 + n;
         mult = ks;
         kind = 2;
-        dst = (char*)(p.seg_out + slot * kKvRank + 4 * g);
+        dst = (char*)(p.seg_out + slot * kKvRank + 16 * db0 + 4 * g);
         stat0 = bad_all ? __builtin_nanf("") : m_fin[q];
         stat0_p = p.seg_max + slot;
         stat1 = l_tot;
         stat1_p = p.seg_sum + slot;
       }
 #pragma unroll
-      for (int db = 0; db < 32; ++db) {
+      for (int db = 0; db < ND; ++db) {
         const f32x4 o = acc[q][db] * mult;
         if (kind == 2) {
           *(f32x4*)(dst + 64 * db) = o;
@@ -734,7 +741,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (g == 0) {
+      if (with_stats && g == 0) {
         *stat0_p = stat0;
         if (stat1_p) *stat1_p = stat1;
       }
@@ -743,6 +750,16 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
 
   if constexpr (!WS) {
     // ---- every wave: QK, softmax and P.V of its own rows, tile after tile ----
+    // k-split waves (KS > 1): wave kw takes tiles first, first + KS, ... of
+    // the piece in its own ring slots kw * NBUF ..; pc.phase rotates the
+    // first tile so that the waves share a workgroup's pieces evenly.
+    static_assert(KS == 1 || (NW == 1 && RG == 1 && CONTIG && NBUF > 1 && 32 % KS == 0),
+                  "k-split waves: one row group over contiguous tiles");
+    const int kw = KS > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+    const int first = KS > 1 ? (kw - pc.phase + KS) % KS : 0;
+    const int nloc = ntiles > first ? (ntiles - first + KS - 1) / KS : 0;
+    const int slot0 = kw * NBUF;
+    auto tile_of = [&](int k) { return first + KS * k; };
     QBf qop;
     QLat qlat;
     QRope qrope;
@@ -759,9 +776,9 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
 
 #pragma unroll
     for (int k = 0; k < NBUF - 1; ++k)
-      if (k < ntiles) issue_tile(k, k);
+      if (k < nloc) issue_tile(tile_of(k), slot0 + k);
 
-    for (int k = 0; k < ntiles; ++k) {
+    for (int k = 0; k < nloc; ++k) {
       if constexpr (NBUF == 1) {
         // Single slot: load, wait, compute; other waves on the SIMD overlap.
         if (k > 0) __syncthreads();  // every wave is done with the slot
@@ -772,20 +789,20 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         // A lone wave owns its ring: the slot of tile k-1 is free as soon as
         // its reads returned, so the next tile is issued before waiting for
         // tile k and NBUF tiles are in flight during the wait.
-        if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
-        wait_tiles<kNIw, NBUF - 1>(min(NBUF - 1, ntiles - 1 - k));
+        if (k + NBUF - 1 < nloc) issue_tile(tile_of(k + NBUF - 1), slot0 + (k + NBUF - 1) % NBUF);
+        wait_tiles<kNIw, NBUF - 1>(min(NBUF - 1, nloc - 1 - k));
       } else {
         wait_tiles<kNIw, (NBUF >= 2 ? NBUF - 2 : 0)>(min(NBUF - 2, ntiles - 1 - k));
         __syncthreads();
         if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
       }
       if (!wave_has_rows) continue;
-      const char* buf = lds[k % NBUF];
+      const char* buf = lds[slot0 + k % NBUF];
       SBlk sblk;
       qk_tile(buf, qop, qlat, qrope, sblk);
       PVal pvv;
       float alpha[RG];
-      const bool resc = softmax_tile(sblk, seg_start + k * TT, m_run, m_true, l_run, pvv, alpha);
+      const bool resc = softmax_tile(sblk, seg_start + tile_of(k) * TT, m_run, m_true, l_run, pvv, alpha);
       if (__ballot(resc)) rescale_acc(acc, alpha);
       __builtin_amdgcn_sched_barrier(0);
       pv_tile(buf, acc, pvv);
@@ -806,7 +823,48 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       l_tot[q] += __shfl_xor(l_tot[q], 32);
     }
     bad = __syncthreads_or(bad ? 1 : 0) != 0;
-    write_result(acc, l_tot, m_true, bad);
+    if constexpr (KS == 1) {
+      write_result(acc, l_tot, m_true, bad, 0, true);
+    } else {
+      // Combine the k-split waves' states: each leaves its rows' max and sum
+      // and its accumulator (scaled to its own max) in its ring slots (whose
+      // DMA and reads are complete); then wave kw sums dim blocks
+      // kDB * kw .. + kDB - 1 over the waves, each weighted by 2^(m_w - M)
+      // for the common max M, and stores them.
+      __shared__ float ks_stat[KS][2][16];
+      constexpr int kDB = 32 / KS;
+      char* own = &lds[slot0][0];
+      if (g == 0) {
+        ks_stat[kw][0][n] = m_true[0];
+        ks_stat[kw][1][n] = l_tot[0];
+      }
+#pragma unroll
+      for (int db = 0; db < 32; ++db) *(LDS_AS f32x4*)(own + 1024 * db + 16 * lane) = acc[0][db];
+      __syncthreads();
+      float m_all = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < KS; ++w) m_all = fmaxf(m_all, ks_stat[w][0][n]);
+      float fw[KS];
+      float l_all = 0.f;
+#pragma unroll
+      for (int w = 0; w < KS; ++w) {
+        const float mw = ks_stat[w][0][n];
+        fw[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - m_all);
+        l_all += fw[w] * ks_stat[w][1][n];
+      }
+      f32x4 comb[1][kDB];
+#pragma unroll
+      for (int j = 0; j < kDB; ++j) {
+        comb[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < KS; ++w)
+          comb[0][j] += fw[w] * lds_load<f32x4>(&lds[w * NBUF][0], 1024 * (kDB * kw + j) + 16 * lane);
+      }
+      const float lt[1] = {l_all};
+      const float mf[1] = {m_all};
+      write_result(comb, lt, mf, bad, kDB * kw, kw == 0);
+      __syncthreads();  // every wave is done with the others' slots
+    }
   } else {
     // ---- specialised waves ----
     // Iteration k (k = -1 .. ntiles-1): the S wave of a row group computes
@@ -818,6 +876,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     // j % NBUF; iteration k refills the slot of tile k - 1 (done with), so
     // tiles k+2 .. k+NBUF-2 stay in flight while k and k+1 are in use.
     static_assert(FP8 ? (kNB == 2) : (kNB == 1), "specialised waves: 8-byte P^T operands");
+    static_assert(KS == 1, "specialised waves take whole tiles");
     __shared__ long ws_p[2][NG][64];
     __shared__ float ws_alpha[2][NG][16];
     __shared__ int ws_flag[2][NG];
@@ -901,7 +960,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         __builtin_amdgcn_sched_barrier(0);
       }
       bad = __syncthreads_or(bad ? 1 : 0) != 0;
-      write_result(acc, l_tot, m_fin, bad);
+      write_result(acc, l_tot, m_fin, bad, 0, true);
     }
   }
 }
@@ -934,7 +993,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
   Piece pc;
   pc.r = r; pc.t0 = t0; pc.qlen = qlen; pc.L = L; pc.row0 = row0;
   pc.seg_start = seg_start; pc.seg_end = min(seg_start + span, L);
-  pc.mode = kOutSegment; pc.s = s; pc.prow0 = 0;
+  pc.mode = kOutSegment; pc.s = s; pc.prow0 = 0; pc.phase = 0;
   run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
 }
 
@@ -974,10 +1033,13 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // boundary leaves base-2 partials in the workgroup's slot 0 (its first piece)
 // or slot 1 (its last piece) for the merge.  Workgroup 0 also stores the
 // per-request unit offsets the merge uses to find the pieces.
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void split_kernel(
+// With KS > 1 k-split waves a workgroup's KS waves share each of its pieces
+// tile by tile (one row group) and combine their states at the piece's end,
+// so a workgroup covers KS times the units with the same number of pieces.
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, int KS>
+__global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void split_kernel(
     SegmentLaunch p) {
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF][TileGeom<FP8, TT>::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[KS * NBUF][TileGeom<FP8, TT>::kTileBytes];
   __shared__ int phys_rows[CONTIG ? 1 : TT];
   constexpr int kRowsWG = 16 * RG * (WS ? NW / 2 : NW);
   const int lane = threadIdx.x & 63;
@@ -1046,7 +1108,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
     pc.mode = (a == 0 && b == nt) ? kOutFinal : kOutSplit;
     pc.s = 0;
     pc.prow0 = ((int64_t)gw * 2 + (pos == s_g ? 0 : 1)) * kRowsWG;
-    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
+    pc.phase = (int)((pos - s_g) % KS);
+    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS, KS>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
     pos += b - a;
   }
 }
@@ -1287,21 +1350,24 @@ hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG, bool WS>
+template <bool FP8, int NW, int RG, bool CONTIG, bool WS, int KS>
 hipError_t launch_split(const SegmentLaunch& a, int grid_wgs, hipStream_t stream) {
   constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG, WS);
   constexpr int kTT = kCfg.tt;
   constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
   constexpr int kRing = kCfg.ring / kTileBytes;
-  hipLaunchKernelGGL((split_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS>), dim3(grid_wgs), dim3(64 * NW),
-                     0, stream, a);
+  hipLaunchKernelGGL((split_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS, KS>), dim3(grid_wgs),
+                     dim3(64 * NW * KS), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool FP8, int NW, int RG, bool CONTIG, bool WS = false>
 hipError_t launch_any(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
-  return split_wgs > 0 ? launch_split<FP8, NW, RG, CONTIG, WS>(a, split_wgs, stream)
-                       : launch_seg<FP8, NW, RG, CONTIG, WS>(a, sh.chunks, stream);
+  if (split_wgs <= 0) return launch_seg<FP8, NW, RG, CONTIG, WS>(a, sh.chunks, stream);
+  if constexpr (NW == 1 && RG == 1 && CONTIG && !WS) {
+    if (sh.ks == kSplitKs) return launch_split<FP8, NW, RG, CONTIG, WS, kSplitKs>(a, split_wgs, stream);
+  }
+  return launch_split<FP8, NW, RG, CONTIG, WS, 1>(a, split_wgs, stream);
 }
 
 template <bool FP8, bool CONTIG>
@@ -1334,6 +1400,7 @@ SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
   const int rows_wg = 16 * sh.rows_per_wave * (sh.ws ? sh.waves / 2 : sh.waves);
   sh.chunks = (max_qlen * num_heads + rows_wg - 1) / rows_wg;
   sh.contig = tile >= tile_tokens(fp8, sh.waves, sh.rows_per_wave, sh.ws);
+  sh.ks = split_ks(sh.waves, sh.rows_per_wave, sh.ws, sh.contig);
   return sh;
 }
 
