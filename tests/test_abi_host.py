@@ -178,6 +178,22 @@ def test_split_plan_shapes():
     assert m.split_plan(_split_problem(H=16))[0] <= 4 * (63 + 1)
 
 
+def test_split_plan_aligns_uniform_batches():
+    # Equal requests: a whole number of workgroups per request (one piece each)
+    # when that keeps >= 3/4 of the slots (one row group) or >= 7/8 (more).
+    # Without a GPU the planner assumes 256 CUs.
+    assert m.split_plan(_split_problem(H=16, R=52, L=200))[0] == 208      # 4 per request
+    assert m.split_plan(_split_problem(H=16, R=100, L=200))[0] == 200     # 2 per request
+    assert m.split_plan(_split_problem(H=16, R=130, L=200))[0] == 256     # 130 < 192: all slots
+    fp8 = torch.float8_e4m3fn
+    assert m.split_plan(_split_problem(H=64, R=52, L=1000, dtype=fp8))[0] == 468  # 9 x 52 of 512
+    assert m.split_plan(_split_problem(H=128, R=52, L=200, block=256))[0] == 256  # 208 < 224
+    # unequal lengths (the summed lengths say so): every slot
+    p = _split_problem(H=16, R=52, L=200)
+    p.sum_seq_lens = 52 * 200 - 1
+    assert m.split_plan(p)[0] == 256
+
+
 def test_split_plan_respects_max_workgroups_and_segment_mode():
     assert m.split_plan(_split_problem(max_workgroups=3))[0] == 3
     assert m.split_plan(_split_problem(max_workgroups=1))[0] == 1
