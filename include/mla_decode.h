@@ -119,6 +119,17 @@ typedef struct mla_problem {
   int32_t max_workgroups; /* balanced split: at most this many workgroups
                              (0 = as many as the device holds at once), e.g.
                              to leave compute units to concurrent work */
+
+  /* Ragged page lists (NULL = the 2-D table above).  When set, device int32
+   * [R+1], non-decreasing: the pages of request r are
+   * block_table[(bt_indptr[r] + i) * bt_stride_col] for i < bt_indptr[r+1] -
+   * bt_indptr[r] (bt_stride_row and max_blocks_per_req are then unused), and a
+   * seq_len past that count times block_size is reported as NaN like a length
+   * past the table.  With block_size 1 this is the index stream of the sparse
+   * MLA page's decode (vLLM API page "rocm_aiter_mla_sparse",
+   * ROCMAiterMLASparseImpl.forward_mqa / _forward_mla: one request per query
+   * token, paged_kv_indptr / paged_kv_indices over a [rows, 1, 576] cache). */
+  const int32_t* bt_indptr;
 } mla_problem;
 
 /*

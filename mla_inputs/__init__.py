@@ -60,6 +60,7 @@ class Workload:
     q_scale: Optional[float] = None  # dequant multiplier (None -> 1.0)
     kv_scale: Optional[float] = None
     sinks: Optional[np.ndarray] = None  # float32 [H]
+    bt_indptr: Optional[np.ndarray] = None  # int32 [R+1]: block_table is one flat page list
     tile_size: int = 0  # 0 -> largest pow2 divisor of block, capped at 128
     num_segments: int = 0  # 0 -> library planner decides
     seed: int = 0
@@ -220,6 +221,65 @@ def make_workload(
 # batch and context so the fp64 oracle finishes in seconds.
 # ---------------------------------------------------------------------------
 
+def as_ragged_pages(w: Workload) -> Workload:
+    """The same batch with its page lists as one flat list plus offsets
+    (``bt_indptr``): request r keeps exactly its cdiv(len, block) pages, so a
+    read past its last page lands on the next request's pages (or, for the
+    last one, past the list)."""
+    B = w.block_size
+    counts = [(int(L) + B - 1) // B for L in w.seq_lens]
+    flat = np.concatenate([w.block_table[r, :c] for r, c in enumerate(counts)] +
+                          [np.zeros(0, dtype=np.int32)]).astype(np.int32)
+    ip = np.zeros(w.num_reqs + 1, dtype=np.int32)
+    ip[1:] = np.cumsum(counts)
+    return with_(w, block_table=flat, bt_indptr=ip, name=w.name + "-ragged-pages")
+
+
+def sparse_batch(*, num_tokens: int, topk: int, ctx: int, num_heads: int, dtype: str = "bf16",
+                 counts=None, sinks: bool = True, seed: int = 0,
+                 name: Optional[str] = None) -> Workload:
+    """Index-stream (sparse top-k) decode batch: token t belongs to a request
+    with ``ctx`` cached positions and attends to ``counts[t]`` (default
+    ``topk``) distinct positions of it, drawn at random.  The cache is a
+    [num_tokens * ctx (+1 poison), 1, 576] view (page size 1) and the block
+    table is the flat index stream with per-token offsets, as the sparse MLA
+    page passes ``paged_kv_indptr`` / ``paged_kv_indices``."""
+    g = _gen(seed)
+    if counts is None:
+        counts = [topk] * num_tokens
+    counts = np.asarray(counts, dtype=np.int64)
+    assert counts.shape == (num_tokens,) and (counts <= ctx).all()
+    rows = num_tokens * ctx
+    kv = torch.randn((rows + 1) * HEAD_DIM, generator=g, dtype=torch.float32).view(rows + 1, 1, HEAD_DIM)
+    q = torch.randn(num_tokens * num_heads * HEAD_DIM, generator=g, dtype=torch.float32)
+    q = q.view(num_tokens, num_heads, HEAD_DIM)
+    kv_codes, kv_scale = _encode(kv, dtype)
+    q_codes, q_scale = _encode(q, dtype)
+    del kv, q
+    kv_codes[rows] = _poison_code(dtype)
+    lists = [(t * ctx + torch.randperm(ctx, generator=g)[: int(c)].numpy()).astype(np.int32)
+             for t, c in enumerate(counts)]
+    flat = np.concatenate(lists + [np.zeros(0, dtype=np.int32)]).astype(np.int32)
+    ip = np.zeros(num_tokens + 1, dtype=np.int32)
+    ip[1:] = np.cumsum(counts)
+    sink_arr = torch.randn(num_heads, generator=g, dtype=torch.float32).numpy() if sinks else None
+    return Workload(
+        name=name or f"sparse_t{num_tokens}_top{topk}_ctx{ctx}_h{num_heads}_{dtype}",
+        num_heads=num_heads, block_size=1, q_dtype=dtype, kv_dtype=dtype, q=q_codes,
+        kv_cache=kv_codes, block_table=flat, seq_lens=counts.astype(np.int32),
+        qo_indptr=np.arange(num_tokens + 1, dtype=np.int32), softmax_scale=1.0 / math.sqrt(192.0),
+        q_scale=q_scale, kv_scale=kv_scale, sinks=sink_arr, bt_indptr=ip, seed=seed,
+        meta={"poison_block": rows})
+
+
+def sparse_bs52(num_heads: int = 16, dtype: str = "bf16", topk: int = 2048, ctx: int = 16384,
+                bs: int = 52) -> Workload:
+    """52 decode tokens, each attending to 2048 of its request's 16384 cached
+    positions (a top-k index stream), sinks on."""
+    return sparse_batch(num_tokens=bs, topk=topk, ctx=ctx, num_heads=num_heads, dtype=dtype,
+                        sinks=True, seed=6 if dtype == "bf16" else 7)
+
+
 def tiny() -> Workload:
     """2 requests, lengths {100, 257}, 16 heads, bf16, page = TILE = 16, S = 4."""
     return make_workload(name="tiny", seq_lens=[100, 257], num_heads=16, block_size=16,
@@ -286,6 +346,7 @@ def to_torch(w: Workload, device="cuda") -> dict:
         "q": codes(w.q, w.q_dtype),
         "kv_cache": codes(w.kv_cache, w.kv_dtype),
         "block_table": torch.from_numpy(np.ascontiguousarray(w.block_table)).to(device),
+        "bt_indptr": None if w.bt_indptr is None else torch.from_numpy(np.ascontiguousarray(w.bt_indptr)).to(device),
         "seq_lens": torch.from_numpy(np.ascontiguousarray(w.seq_lens)).to(device),
         "qo_indptr": torch.from_numpy(np.ascontiguousarray(w.qo_indptr)).to(device),
         "q_scale": None if w.q_scale is None else torch.tensor([w.q_scale], dtype=torch.float32, device=device),
@@ -304,4 +365,5 @@ def call_args(w: Workload, d: dict, *, use_indptr: Optional[bool] = None) -> dic
                 max_seq_len=w.max_seq_len, qo_indptr=d["qo_indptr"] if use_indptr else None,
                 max_qlen=w.max_qlen if use_indptr else None, causal=w.causal,
                 q_scale=d["q_scale"], kv_scale=d["kv_scale"], tile_size=w.tile_size,
+                bt_indptr=d.get("bt_indptr"),
                 sum_seq_lens=int(np.asarray(w.seq_lens, dtype=np.int64).sum()))

@@ -78,6 +78,7 @@ class MlaProblem(ctypes.Structure):
         ("tile_size", ctypes.c_int32),
         ("num_segments", ctypes.c_int32),
         ("max_workgroups", ctypes.c_int32),
+        ("bt_indptr", ctypes.c_void_p),
     ]
 
 
@@ -202,9 +203,14 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
                  qo_indptr: Optional[torch.Tensor] = None, max_qlen: Optional[int] = None,
                  causal: bool = False, q_scale: Optional[torch.Tensor] = None,
                  kv_scale: Optional[torch.Tensor] = None, tile_size: int = 0,
-                 num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0) -> MlaProblem:
+                 num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0,
+                 bt_indptr: Optional[torch.Tensor] = None) -> MlaProblem:
     """Fill an ``mla_problem`` from tensors.  Host ints (max_seq_len, max_qlen)
-    are passed by the caller so nothing is read back from the device."""
+    are passed by the caller so nothing is read back from the device.
+
+    With ``bt_indptr`` (int32 [R+1]) the block table is one flat int32 list and
+    request r's pages are ``block_table[bt_indptr[r]:bt_indptr[r+1]]``; with
+    block_size 1 that is a per-token index stream (sparse decode)."""
     if q.ndim != 3 or q.shape[-1] != HEAD_DIM or q.stride(-1) != 1:
         raise ValueError(f"q must be [T, H, 576] with a contiguous last dim, got {tuple(q.shape)}")
     if kv_cache.ndim != 3 or kv_cache.shape[-1] != HEAD_DIM or not kv_cache.is_contiguous():
@@ -215,6 +221,13 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
                          "(bf16 with bf16, fp8 with fp8)")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
+    if bt_indptr is not None:
+        if bt_indptr.dtype != torch.int32 or bt_indptr.shape != (seq_lens.shape[0] + 1,):
+            raise ValueError("bt_indptr must be int32 [num_reqs + 1]")
+        if block_table.ndim != 1:
+            raise ValueError("with bt_indptr the block table is one flat int32 list")
+    elif block_table.ndim != 2:
+        raise ValueError("block_table must be int32 [num_reqs, max_blocks_per_req]")
     if qo_indptr is not None and qo_indptr.dtype != torch.int32:
         raise ValueError("qo_indptr must be int32")
     for name, s in (("q_scale", q_scale), ("kv_scale", kv_scale)):
@@ -232,8 +245,13 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
     p.block_size, p.num_blocks = kv_cache.shape[1], kv_cache.shape[0]
     p.kv_scale = _ptr(kv_scale)
     p.block_table = _ptr(block_table)
-    p.bt_stride_row, p.bt_stride_col = block_table.stride(0), block_table.stride(1)
-    p.max_blocks_per_req = block_table.shape[1]
+    if bt_indptr is not None:
+        p.bt_stride_row, p.bt_stride_col = 0, block_table.stride(0)
+        p.max_blocks_per_req = 0
+        p.bt_indptr = _ptr(bt_indptr)
+    else:
+        p.bt_stride_row, p.bt_stride_col = block_table.stride(0), block_table.stride(1)
+        p.max_blocks_per_req = block_table.shape[1]
     p.seq_lens = _ptr(seq_lens)
     p.qo_indptr = _ptr(qo_indptr)
     p.max_qlen = 1 if qo_indptr is None else int(max_qlen if max_qlen is not None else 1)
@@ -274,13 +292,13 @@ def workspace_bytes(p: MlaProblem) -> int:
 def decode_segments(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, num_segments: int,
                     max_seq_len: int, qo_indptr=None, max_qlen=None, causal=False, q_scale=None,
                     kv_scale=None, tile_size: int = 0, sum_seq_lens: int = 0, segm_output=None,
-                    segm_max=None, segm_expsum=None, stream=None):
+                    segm_max=None, segm_expsum=None, bt_indptr=None, stream=None):
     """Base-2 partials [T, H, S, 512], [T, H, S], [T, H, S] (fp32).  Slots of
     segments that hold no position are left as allocated (uninitialised)."""
     p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                      max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen, causal=causal,
                      q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size, num_segments=num_segments,
-                     sum_seq_lens=sum_seq_lens)
+                     sum_seq_lens=sum_seq_lens, bt_indptr=bt_indptr)
     T, H, S = q.shape[0], q.shape[1], int(num_segments)
     dev = q.device
     if segm_output is None:
@@ -317,12 +335,13 @@ def merge_segments(segm_output, segm_max, segm_expsum, part_lens, tile_size: int
 def decode(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_len: int,
            qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
            tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0,
-           out_dtype=torch.bfloat16, out=None, lse=None, workspace=None, stream=None):
+           out_dtype=torch.bfloat16, out=None, lse=None, workspace=None, bt_indptr=None, stream=None):
     """Fused decode: returns (out [T, H, 512], lse [T, H])."""
     p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                      max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen, causal=causal,
                      q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
-                     num_segments=num_segments, sum_seq_lens=sum_seq_lens, max_workgroups=max_workgroups)
+                     num_segments=num_segments, sum_seq_lens=sum_seq_lens, max_workgroups=max_workgroups,
+                     bt_indptr=bt_indptr)
     T, H = q.shape[0], q.shape[1]
     check_sinks(sinks, H)
     if out is None:
@@ -350,12 +369,12 @@ class Decoder:
     def __init__(self, q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_len: int,
                  qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
                  tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0,
-                 max_workgroups: int = 0, out_dtype=torch.bfloat16):
+                 max_workgroups: int = 0, out_dtype=torch.bfloat16, bt_indptr=None):
         self.p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                               max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen,
                               causal=causal, q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
                               num_segments=num_segments, sum_seq_lens=sum_seq_lens,
-                              max_workgroups=max_workgroups)
+                              max_workgroups=max_workgroups, bt_indptr=bt_indptr)
         check_sinks(sinks, q.shape[1])
         # num_segments == 0 keeps the balanced split (split_workgroups > 0);
         # otherwise the segment partition with that S.
@@ -367,7 +386,7 @@ class Decoder:
         self.out = torch.empty((T, H, KV_LORA_RANK), dtype=out_dtype, device=q.device)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
         self.workspace = torch.empty(max(workspace_bytes(self.p), 256), dtype=torch.uint8, device=q.device)
-        self._keep = (q, kv_cache, block_table, seq_lens, qo_indptr, q_scale, kv_scale, sinks)
+        self._keep = (q, kv_cache, block_table, seq_lens, qo_indptr, q_scale, kv_scale, sinks, bt_indptr)
         self._fn = lib().mla_decode
         self._args = (ctypes.byref(self.p), _ptr(sinks), _ptr(self.out), _out_code(out_dtype), _ptr(self.lse),
                       _ptr(self.workspace), self.workspace.numel())

@@ -129,12 +129,14 @@ int validate(const mla_problem* p, bool require_segments) {
     return fail(MLA_ERR_INVALID_ARG,
                 "q strides (token %lld, head %lld elements) must be >= 0 / >= 576 and multiples of 16 bytes",
                 (long long)p->q_stride_token, (long long)p->q_stride_head);
-  if (p->max_blocks_per_req < 1) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_req must be >= 1");
-  if (cdiv64(p->max_seq_len, p->block_size) > p->max_blocks_per_req)
-    return fail(MLA_ERR_INVALID_ARG, "max_seq_len %d needs %lld blocks but the table has %d columns",
-                p->max_seq_len, (long long)cdiv64(p->max_seq_len, p->block_size), p->max_blocks_per_req);
-  if ((int64_t)p->max_blocks_per_req * p->block_size >= ((int64_t)1 << 31))
-    return fail(MLA_ERR_UNSUPPORTED, "block table spans more than 2^31 positions");
+  if (!p->bt_indptr) {
+    if (p->max_blocks_per_req < 1) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_req must be >= 1");
+    if (cdiv64(p->max_seq_len, p->block_size) > p->max_blocks_per_req)
+      return fail(MLA_ERR_INVALID_ARG, "max_seq_len %d needs %lld blocks but the table has %d columns",
+                  p->max_seq_len, (long long)cdiv64(p->max_seq_len, p->block_size), p->max_blocks_per_req);
+    if ((int64_t)p->max_blocks_per_req * p->block_size >= ((int64_t)1 << 31))
+      return fail(MLA_ERR_UNSUPPORTED, "block table spans more than 2^31 positions");
+  }
   if (p->bt_stride_col < 1 || p->bt_stride_row < 0)
     return fail(MLA_ERR_INVALID_ARG, "block_table strides must be row >= 0, col >= 1");
   return MLA_OK;
@@ -250,6 +252,7 @@ mla::SegmentLaunch make_launch(const mla_problem* p, int tile, int S, float* so,
   a.bt_stride_row = p->bt_stride_row;
   a.bt_stride_col = p->bt_stride_col;
   a.bt_cols = p->max_blocks_per_req;
+  a.bt_indptr = p->bt_indptr;
   a.seq_lens = p->seq_lens;
   a.qo_indptr = p->qo_indptr;
   a.num_tokens = p->num_tokens;

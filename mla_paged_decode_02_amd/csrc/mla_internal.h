@@ -58,6 +58,7 @@ struct SegmentLaunch {
   const int32_t* block_table;
   int64_t bt_stride_row, bt_stride_col;
   int32_t bt_cols;
+  const int32_t* bt_indptr;  // nullable: ragged page lists (block_table is then flat)
   const int32_t* seq_lens;
   const int32_t* qo_indptr;  // nullable -> one token per request
   int32_t num_tokens, num_heads, num_reqs, max_qlen;

@@ -197,6 +197,22 @@ struct Piece {
   int64_t prow0;   // first partial row of the piece (kOutSplit)
   int phase;       // k-split waves: the wave that takes the piece's first tile
 };
+
+// Where request r's pages start in the block table, and how many positions
+// they cover: row r of the 2-D table, or (ragged lists) the flat range
+// [bt_indptr[r], bt_indptr[r+1]).  Uniform loads of read-only data.
+__device__ __forceinline__ void page_list(const SegmentLaunch& p, int r, int64_t* base, int* cap) {
+  if (p.bt_indptr) {
+    const __attribute__((address_space(4))) int* ip = (const __attribute__((address_space(4))) int*)p.bt_indptr;
+    const int a = ip[r], b = ip[r + 1];
+    *base = (int64_t)a * p.bt_stride_col;
+    const int64_t c = (int64_t)(b - a) * p.block_size;
+    *cap = c < 0 ? 0 : (c > 0x7fffffff ? 0x7fffffff : (int)c);
+  } else {
+    *base = (int64_t)r * p.bt_stride_row;
+    *cap = p.bt_cols * p.block_size;
+  }
+}
 // Where a piece's result goes:
 //  segment: base-2 partials of segment s at [t, h, s] of the segment buffers;
 //  final:   the piece is a whole (request, row chunk): normalised output and
@@ -263,7 +279,12 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   const int row0 = pc.row0;
   // A length past the block table is reported as NaN; rows beyond the table
   // are never read.
-  const int cap = p.bt_cols * p.block_size;
+  int64_t bt_base;
+  int cap;
+  page_list(p, r, &bt_base, &cap);
+  bt_base = __builtin_amdgcn_readfirstlane((int)(bt_base & 0xffffffff)) |
+            ((int64_t)__builtin_amdgcn_readfirstlane((int)(bt_base >> 32)) << 32);
+  cap = __builtin_amdgcn_readfirstlane(cap);
   bool bad = L > cap;
   const int seg_start = pc.seg_start;
   const int seg_end = pc.seg_end;
@@ -352,7 +373,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       // address space, so no vector-memory wait drains the DMA stream.
       const int blk_i = tile_start / p.block_size;
       int blk = ((const __attribute__((address_space(4))) int*)p.block_table)
-          [(int64_t)r * p.bt_stride_row + (int64_t)blk_i * p.bt_stride_col];
+          [bt_base + (int64_t)blk_i * p.bt_stride_col];
       if (blk < 0 || blk >= p.num_blocks) { blk = 0; bad = true; }
       const int64_t phys0 = (int64_t)blk * p.block_size + (tile_start - blk_i * p.block_size);
       // Buffer descriptor over the tile's 32 rows (a guard: no offset below
@@ -394,7 +415,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       if (threadIdx.x < TT) {
         const int j = tile_start + ((int)threadIdx.x < nvalid ? (int)threadIdx.x : 0);
         const int blk_i = j / p.block_size;
-        const int blk = p.block_table[(int64_t)r * p.bt_stride_row + (int64_t)blk_i * p.bt_stride_col];
+        const int blk = p.block_table[bt_base + (int64_t)blk_i * p.bt_stride_col];
         phys_rows[threadIdx.x] =
             (blk < 0 || blk >= p.num_blocks) ? -1 : blk * p.block_size + (j - blk_i * p.block_size);
       }

@@ -168,6 +168,17 @@ def subpage_table(block_table: np.ndarray, block_size: int, tile_size: int) -> n
     return (bt[:, :, None] * ppb + np.arange(ppb)[None, None, :]).reshape(bt.shape[0], -1)
 
 
+def pages_of(block_table: np.ndarray, bt_indptr: Optional[np.ndarray], r: int) -> np.ndarray:
+    """Request r's page list: row r of a [R, max_blocks] table, or with
+    ``bt_indptr`` the slice [bt_indptr[r], bt_indptr[r+1]) of a flat list.
+    With page size 1 the flat form is the per-token index stream of [sparse
+    page] ``_forward_mla`` (``paged_kv_indptr`` / ``paged_kv_indices`` over a
+    [rows, 1, 576] cache view)."""
+    if bt_indptr is None:
+        return block_table[r]
+    return block_table[int(bt_indptr[r]):int(bt_indptr[r + 1])]
+
+
 def gather_rows(kv_flat: np.ndarray, block_table_row: np.ndarray, n: int,
                 block_size: int) -> np.ndarray:
     """Rows of the first n positions of one request, in logical order."""
@@ -220,6 +231,7 @@ class DecodedBatch:
     q: np.ndarray
     kv_flat: np.ndarray
     block_table: np.ndarray
+    bt_indptr: Optional[np.ndarray]
     seq_lens: np.ndarray
     qo_indptr: np.ndarray
     block_size: int
@@ -242,10 +254,12 @@ def decode_workload(w, reqs: Optional[Sequence[int]] = None) -> DecodedBatch:
             n = int(w.seq_lens[r])
             if n == 0:
                 continue
-            idx = np.array([cache_row_index(w.block_table[r], j, bsz) for j in range(n)])
+            pages = pages_of(np.asarray(w.block_table), w.bt_indptr, r)
+            idx = np.array([cache_row_index(pages, j, bsz) for j in range(n)])
             kv_flat[idx] = decode(flat[idx], w.kv_dtype, w.kv_scale)
     q = decode(np.asarray(w.q), w.q_dtype, w.q_scale)
     return DecodedBatch(q=q, kv_flat=kv_flat, block_table=np.asarray(w.block_table),
+                        bt_indptr=None if w.bt_indptr is None else np.asarray(w.bt_indptr),
                         seq_lens=np.asarray(w.seq_lens), qo_indptr=np.asarray(w.qo_indptr),
                         block_size=bsz, scale=float(w.softmax_scale), causal=bool(w.causal),
                         sinks=None if w.sinks is None else np.asarray(w.sinks, np.float64))
@@ -265,7 +279,7 @@ def mla_decode(w, reqs: Optional[Sequence[int]] = None,
         t0, t1 = int(db.qo_indptr[r]), int(db.qo_indptr[r + 1])
         qlen = t1 - t0
         L = int(db.seq_lens[r])
-        rows = gather_rows(db.kv_flat, db.block_table[r], L, db.block_size)
+        rows = gather_rows(db.kv_flat, pages_of(db.block_table, db.bt_indptr, r), L, db.block_size)
         for i in range(qlen):
             n = visible_len(L, qlen, i, db.causal)
             o, l = attend(db.q[t0 + i], rows[:n], db.scale, db.sinks)
@@ -322,7 +336,7 @@ def mla_decode_segments(w, num_segments: int, tile_size: int,
         t0, t1 = int(db.qo_indptr[r]), int(db.qo_indptr[r + 1])
         qlen = t1 - t0
         L = int(db.seq_lens[r])
-        rows = gather_rows(db.kv_flat, db.block_table[r], L, db.block_size)
+        rows = gather_rows(db.kv_flat, pages_of(db.block_table, db.bt_indptr, r), L, db.block_size)
         bounds = segment_bounds(L, S, tile_size)
         for i in range(qlen):
             t = t0 + i

@@ -26,7 +26,8 @@ def vmax(w, reqs=None) -> float:
         n = int(w.seq_lens[r])
         if n == 0:
             continue
-        idx = np.array([orc.cache_row_index(w.block_table[r], j, bsz) for j in range(n)])
+        pages = orc.pages_of(np.asarray(w.block_table), w.bt_indptr, r)
+        idx = np.array([orc.cache_row_index(pages, j, bsz) for j in range(n)])
         v = orc.decode(flat[idx][:, :512], w.kv_dtype, w.kv_scale)
         best = max(best, float(np.abs(v).max()))
     return best

@@ -113,6 +113,27 @@ def test_validate_rejects(field, value, code):
     assert len(m.lib().mla_last_error().decode()) > 0
 
 
+def test_ragged_page_lists_validate():
+    """With bt_indptr the table is one flat list: the 2-D column bound does
+    not apply, and the Python wrapper checks the shapes."""
+    q = torch.zeros((3, 16, 576), dtype=torch.bfloat16)
+    kv = torch.zeros((40, 1, 576), dtype=torch.bfloat16)
+    flat = torch.zeros(25, dtype=torch.int32)
+    ip = torch.tensor([0, 10, 10, 25], dtype=torch.int32)
+    sl = torch.tensor([10, 0, 15], dtype=torch.int32)
+    p = m.make_problem(q, kv, flat, sl, softmax_scale=0.1, max_seq_len=15, num_segments=2, bt_indptr=ip)
+    assert p.max_blocks_per_req == 0 and p.bt_stride_col == 1 and p.bt_indptr
+    assert _status(p) == m.MLA_OK
+    p.bt_indptr = None  # the same problem as a 2-D table has no columns
+    assert _status(p) == m.MLA_ERR_INVALID_ARG
+    with pytest.raises(ValueError, match="flat"):
+        m.make_problem(q, kv, flat.view(5, 5), sl, softmax_scale=0.1, max_seq_len=15, bt_indptr=ip)
+    with pytest.raises(ValueError, match="bt_indptr"):
+        m.make_problem(q, kv, flat, sl, softmax_scale=0.1, max_seq_len=15, bt_indptr=ip[:3])
+    with pytest.raises(ValueError, match="block_table"):
+        m.make_problem(q, kv, flat, sl, softmax_scale=0.1, max_seq_len=15)
+
+
 def test_decode_entry_points_fail_before_launch():
     """Invalid arguments return an error from every entry point without
     touching the device (this test runs without a GPU)."""

@@ -1,7 +1,7 @@
 """Parity at full size, in the launch configuration the benchmark times.
 
-Each workload is built at its real shape (52 requests x 16384 tokens, or the
-128-request ragged causal batch) and decoded on the GPU with the planner's
+Each workload is built at its real shape (52 requests x 16384 tokens, the
+128-request ragged causal batch, or 52 index-stream tokens of 2048 rows) and decoded on the GPU with the planner's
 default split through one prepared ``mla_decode`` call, bf16 output (the
 same call ``bench.py`` times).  The fp64 oracle then computes a sample of the
 requests one by one, and the outputs of every token row of those requests are
@@ -26,6 +26,8 @@ FULL = {
     "bs52_ctx16k_h64_fp8_blk64": lambda: mi.bs52_fp8(64),
     "bs52_ctx16k_h128_bf16_blk256": lambda: mi.bs52_h128_bf16(),
     "ragged128_max32k_h96_fp8_causal_sinks": lambda: mi.ragged_h96_fp8(),
+    "sparse_bs52_top2048_ctx16k_h16_bf16": lambda: mi.sparse_bs52(16, "bf16"),
+    "sparse_bs52_top2048_ctx16k_h128_fp8": lambda: mi.sparse_bs52(128, "fp8_e4m3"),
 }
 
 

@@ -426,3 +426,45 @@ def test_poison_pages_not_read():
     assert np.any(np.isnan(orc.decode_bf16(flat)))
     o, l = orc.mla_decode(w)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+# ------------------------------------------------- ragged page lists ----
+
+def test_ragged_page_lists_reach_the_same_rows():
+    """The flat page list + offsets form of a batch names the same cache rows
+    as its 2-D table, position by position (so the oracle's result is the
+    same), and the list ends exactly at each request's last page."""
+    w = mi.make_workload(name="rp", seq_lens=[5, 17, 64, 0, 33], num_heads=2, block_size=16,
+                         dtype="bf16", seed=25, extra_bt_cols=2)
+    wr = mi.as_ragged_pages(w)
+    assert wr.block_table.ndim == 1 and wr.bt_indptr[-1] == wr.block_table.shape[0]
+    for r, L in enumerate(w.seq_lens):
+        pages = orc.pages_of(wr.block_table, wr.bt_indptr, r)
+        assert len(pages) == (int(L) + 15) // 16
+        for j in range(int(L)):
+            assert orc.cache_row_index(pages, j, 16) == orc.cache_row_index(w.block_table[r], j, 16)
+    o1, l1 = orc.mla_decode(w)
+    o2, l2 = orc.mla_decode(wr)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_sparse_index_stream_is_attention_over_the_listed_rows():
+    """Page size 1 + flat index lists: token t attends exactly to the rows its
+    list names.  Checked against numpy fancy indexing of the decoded cache
+    (no page walk) and torch's logsumexp, with the sink as an extra logit."""
+    w = mi.sparse_batch(num_tokens=4, topk=9, ctx=20, num_heads=3, dtype="bf16",
+                        counts=[9, 0, 1, 5], seed=26)
+    o, l = orc.mla_decode(w)
+    kv = orc.decode_bf16(w.kv_cache.reshape(-1, 576)).astype(np.float64)
+    q = orc.decode_bf16(w.q).astype(np.float64)
+    for t in range(4):
+        idx = w.block_table[w.bt_indptr[t]:w.bt_indptr[t + 1]]
+        assert len(idx) == w.seq_lens[t] and np.all(idx // 20 == t)   # rows of the token's own request
+        rows = kv[idx]
+        s = w.softmax_scale * (q[t] @ rows.T)                           # [H, n]
+        logits = np.concatenate([s, np.asarray(w.sinks, np.float64)[:, None]], axis=1)
+        lse = torch.logsumexp(torch.from_numpy(logits), dim=1).numpy()
+        p = np.exp(s - lse[:, None])
+        assert np.allclose(l[t], lse, atol=1e-12, rtol=0)
+        assert np.allclose(o[t], p @ rows[:, :512], atol=1e-12, rtol=0)
+    assert np.all(o[1] == 0) and np.allclose(l[1], w.sinks, atol=0)  # empty list: sink only
