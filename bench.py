@@ -101,6 +101,59 @@ def warmup(fn, n, torch):
     return time.perf_counter() - t0
 
 
+DCP_WORKLOADS = {
+    # decode context parallelism emulated on one GPU: (shards, base batch)
+    "dcp4_bs52_ctx16k_h16_bf16_blk64": (4, lambda mi: mi.bs52_h16_bf16()),
+}
+
+
+def time_dcp(name, args, torch, m, mi):
+    """One rank's share of a DCP step (its shard's decode + the LSE combine of
+    every shard's output) and the whole step emulated on one GPU (every shard's
+    decode, then the combine)."""
+    W, ctor = DCP_WORKLOADS[name]
+    w = ctor(mi)
+    shards = mi.dcp_shards(w, W)
+    ds = [mi.to_torch(sw, "cuda") for sw in shards]
+    T, H = w.num_tokens, w.num_heads
+    so = torch.empty((W, T, H, 512), dtype=torch.bfloat16, device="cuda")
+    sl = torch.empty((W, T, H), dtype=torch.float32, device="cuda")
+    # each shard decodes straight into its slice of the stacked buffers
+    decs = [m.Decoder(**mi.call_args(sw, d), sinks=None, num_segments=0, out=so[k], lse=sl[k])
+            for k, (sw, d) in enumerate(zip(shards, ds))]
+    sinks = torch.randn(H, generator=torch.Generator().manual_seed(11)).cuda()
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def combine():
+        m.combine_lse(so, sl, sinks=sinks, out=out, lse=lse, stream=stream)
+
+    def timed(fn):
+        warmup(lambda i: fn(), args.warmup, torch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3
+
+    for dec in decs:
+        dec.run(stream)
+    t_rank_decode = timed(lambda: decs[0].run(stream))
+    t_combine = timed(combine)
+    t_step = timed(lambda: ([d.run(stream) for d in decs], combine()))
+    kv_bytes = w.kv_bytes_touched()
+    return {"workload": name, "num_shards": W, "num_heads": H, "dtype": w.kv_dtype,
+            "num_reqs": w.num_reqs, "max_seq_len": w.max_seq_len,
+            "shard_decode_us": round(t_rank_decode, 2), "combine_us": round(t_combine, 2),
+            "rank_step_us": round(t_rank_decode + t_combine, 2),
+            "emulated_step_us": round(t_step, 2),
+            "eff_kv_GBps_emulated": kv_bytes / (t_step * 1e-6) / 1e9,
+            "split_workgroups": decs[0].split_workgroups}
+
+
 def time_workload(name, args, torch, m, mi, want_roofline):
     w, ds = build_inputs(name, torch, mi)
     esz = 2 if w.kv_dtype == "bf16" else 1
@@ -304,6 +357,9 @@ def main():
             torch.cuda.empty_cache()
             _, r2, _ = time_workload(name, args, torch, m, mi, want_roofline=False)
             extra.append(r2)
+        for name in DCP_WORKLOADS:
+            torch.cuda.empty_cache()
+            extra.append(time_dcp(name, args, torch, m, mi))
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_reqs)
     line = {
         "metric": METRIC,

@@ -174,6 +174,27 @@ int mla_merge_segments(const float* segm_output, const float* segm_max, const fl
                        void* stream);
 
 /*
+ * Cross-shard combine for decode context parallelism (the cross-rank merge
+ * that consumes the natural-log LSE of the merge page's module description;
+ * vLLM API page "rocm_aiter_mla" DCP decode routing: token t of a request on
+ * shard t % W, partial outputs merged by LSE).  Shard w computed (out_w, lse_w)
+ * over its keys with mla_decode (without sinks).  For each (t, h):
+ *   lse = ln sum_w e^(lse_w)            (shards with lse_w = -inf add nothing)
+ *   out = sum_w out_w e^(lse_w - lse)
+ * then, with sinks (device fp32 [H] or NULL), once for the whole row:
+ *   lse' = logaddexp(lse, sink[h]), out' = out e^(lse - lse')
+ * A row that no shard saw gets out = 0, lse = -inf (or the sink); a NaN lse_w
+ * makes the row NaN.
+ *  shard_out: device [W, T, H, 512] of in_dtype (BF16, FP16 or FP32),
+ *             contiguous, 16-byte aligned;  shard_lse: device fp32 [W, T, H].
+ *  out: device [T, H, 512] of out_dtype;  lse: device fp32 [T, H].
+ *  1 <= num_shards <= 64.  One stream-ordered launch, no allocation.
+ */
+int mla_combine_lse(const void* shard_out, int32_t in_dtype, const float* shard_lse, int32_t num_shards,
+                    int32_t num_tokens, int32_t num_heads, const float* sinks, void* out,
+                    int32_t out_dtype, float* lse, void* stream);
+
+/*
  * Fused decode: out [T, H, 512] and lse [T, H] in two stream-ordered
  * launches, partial results living in the caller's workspace
  * (>= mla_decode_workspace_bytes(p) bytes, 256-byte aligned; its contents on

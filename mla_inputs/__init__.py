@@ -280,6 +280,65 @@ def sparse_bs52(num_heads: int = 16, dtype: str = "bf16", topk: int = 2048, ctx:
                         sinks=True, seed=6 if dtype == "bf16" else 7)
 
 
+def dcp_shards(w: Workload, num_shards: int) -> list:
+    """Key shards of a batch as decode context parallelism lays them out:
+    position t of a request lives on shard t % W at local position t // W,
+    in local pages of the same block size (a fresh random page permutation
+    per shard, NaN-poisoned tails).  Shards carry no sinks (the combine
+    applies them once).
+
+    Plain route (qlen 1, or no causal mask): the shard keeps the batch's
+    requests, each with its local key count.  Causal blocks of qlen > 1 take
+    the segmented route of the backend page's DCP routing note: every query
+    token becomes its own one-token request whose length is the number of
+    local keys inside its causal window."""
+    W = int(num_shards)
+    B = w.block_size
+    flat = w.kv_cache.reshape(-1, HEAD_DIM)
+    qo = np.asarray(w.qo_indptr)
+    qlens = np.diff(qo)
+    segmented = bool(w.causal) and w.num_reqs > 0 and int(qlens.max()) > 1
+    shards = []
+    g = _gen(w.seed + 77)
+    for s in range(W):
+        local = [max(0, -(-(int(L) - s) // W)) for L in w.seq_lens]   # keys t < L with t % W == s
+        pages = [(n + B - 1) // B for n in local]
+        n_pages = int(sum(pages))
+        perm = torch.randperm(n_pages, generator=g).numpy() if n_pages else np.zeros(0, dtype=np.int64)
+        cache = np.empty((n_pages + 1, B, HEAD_DIM), dtype=w.kv_cache.dtype)
+        cache[:] = _poison_code(w.kv_dtype)
+        bt = np.full((w.num_reqs, max(max(pages, default=1), 1)), n_pages, dtype=np.int32)
+        cur = 0
+        for r in range(w.num_reqs):
+            bt[r, :pages[r]] = perm[cur:cur + pages[r]]
+            cur += pages[r]
+            src_pages = w.block_table[r] if w.bt_indptr is None else \
+                w.block_table[int(w.bt_indptr[r]):int(w.bt_indptr[r + 1])]
+            j = np.arange(local[r], dtype=np.int64)
+            t = j * W + s
+            src = np.asarray(src_pages, dtype=np.int64)[t // B] * B + t % B
+            cache.reshape(-1, HEAD_DIM)[bt[r, j // B].astype(np.int64) * B + j % B] = flat[src]
+        if not segmented:
+            sw = replace(w, kv_cache=cache, block_table=bt, bt_indptr=None,
+                         seq_lens=np.asarray(local, dtype=np.int32), sinks=None,
+                         name=f"{w.name}-dcp{W}.{s}", meta={"poison_block": n_pages})
+        else:
+            T = w.num_tokens
+            row_bt = np.empty((T, bt.shape[1]), dtype=np.int32)
+            row_len = np.zeros(T, dtype=np.int32)
+            for r in range(w.num_reqs):
+                L, ql = int(w.seq_lens[r]), int(qlens[r])
+                for i in range(ql):
+                    vis = max(0, L - ql + i + 1)              # global causal window of token i
+                    row_len[qo[r] + i] = max(0, -(-(vis - s) // W))
+                    row_bt[qo[r] + i] = bt[r]
+            sw = replace(w, kv_cache=cache, block_table=row_bt, bt_indptr=None, seq_lens=row_len,
+                         qo_indptr=np.arange(T + 1, dtype=np.int32), causal=False, sinks=None,
+                         name=f"{w.name}-dcp{W}.{s}", meta={"poison_block": n_pages})
+        shards.append(sw)
+    return shards
+
+
 def tiny() -> Workload:
     """2 requests, lengths {100, 257}, 16 heads, bf16, page = TILE = 16, S = 4."""
     return make_workload(name="tiny", seq_lens=[100, 257], num_heads=16, block_size=16,

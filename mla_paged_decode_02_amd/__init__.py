@@ -88,7 +88,7 @@ EXPORTED = (
     "mla_validate", "mla_decode_segments", "mla_merge_segments", "mla_decode",
     "mla_decode_workspace_bytes", "mla_resolve_num_segments", "mla_plan_num_segments",
     "mla_tile_size_for_block", "mla_segment_bounds", "mla_status_string", "mla_last_error",
-    "mla_version", "mla_decode_stage", "mla_split_plan",
+    "mla_version", "mla_decode_stage", "mla_split_plan", "mla_combine_lse",
 )
 
 
@@ -107,6 +107,7 @@ def lib() -> ctypes.CDLL:
     L.mla_merge_segments.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp]
     L.mla_decode.argtypes = [P, vp, vp, i32, vp, vp, sz, vp]
     L.mla_decode_stage.argtypes = [P, vp, vp, i32, vp, vp, sz, i32, vp]
+    L.mla_combine_lse.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, i32, vp, vp]
     L.mla_split_plan.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.mla_decode_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     L.mla_resolve_num_segments.argtypes = [P]
@@ -121,7 +122,7 @@ def lib() -> ctypes.CDLL:
     for f in ("mla_validate", "mla_decode_segments", "mla_merge_segments", "mla_decode",
               "mla_decode_workspace_bytes", "mla_resolve_num_segments", "mla_plan_num_segments",
               "mla_tile_size_for_block", "mla_segment_bounds", "mla_version", "mla_decode_stage",
-              "mla_split_plan"):
+              "mla_split_plan", "mla_combine_lse"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -357,6 +358,27 @@ def decode(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_
     return out, lse
 
 
+def combine_lse(shard_out, shard_lse, *, sinks=None, out_dtype=torch.bfloat16, out=None, lse=None,
+                stream=None):
+    """Cross-shard combine (decode context parallelism): shard_out
+    [W, T, H, 512] (bf16 / fp16 / fp32) and shard_lse [W, T, H] fp32 from W
+    sink-free decodes of disjoint key shards -> (out [T, H, 512], lse [T, H]),
+    with the sinks applied once to the combined rows."""
+    if shard_out.ndim != 4 or shard_out.shape[-1] != KV_LORA_RANK or not shard_out.is_contiguous():
+        raise ValueError(f"shard_out must be a contiguous [W, T, H, 512] tensor, got {tuple(shard_out.shape)}")
+    W, T, H, _ = shard_out.shape
+    if shard_lse.shape != (W, T, H) or shard_lse.dtype != torch.float32 or not shard_lse.is_contiguous():
+        raise ValueError("shard_lse must be a contiguous float32 [W, T, H] tensor")
+    check_sinks(sinks, H)
+    if out is None:
+        out = torch.empty((T, H, KV_LORA_RANK), dtype=out_dtype, device=shard_out.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=shard_out.device)
+    _check(lib().mla_combine_lse(_ptr(shard_out), _out_code(shard_out.dtype), _ptr(shard_lse), W, T, H,
+                                 _ptr(sinks), _ptr(out), _out_code(out.dtype), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
 class Decoder:
     """A prepared ``mla_decode`` call for a fixed batch layout.
 
@@ -369,7 +391,7 @@ class Decoder:
     def __init__(self, q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_len: int,
                  qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
                  tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0,
-                 max_workgroups: int = 0, out_dtype=torch.bfloat16, bt_indptr=None):
+                 max_workgroups: int = 0, out_dtype=torch.bfloat16, bt_indptr=None, out=None, lse=None):
         self.p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                               max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen,
                               causal=causal, q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
@@ -383,8 +405,13 @@ class Decoder:
         self.num_segments = 0 if self.split else resolve_num_segments(self.p)
         self.p.num_segments = self.num_segments
         T, H = q.shape[0], q.shape[1]
-        self.out = torch.empty((T, H, KV_LORA_RANK), dtype=out_dtype, device=q.device)
-        self.lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+        # out / lse may be given (e.g. one shard's slice of a stacked buffer)
+        self.out = torch.empty((T, H, KV_LORA_RANK), dtype=out_dtype, device=q.device) if out is None else out
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=q.device) if lse is None else lse
+        if tuple(self.out.shape) != (T, H, KV_LORA_RANK) or not self.out.is_contiguous() or \
+                tuple(self.lse.shape) != (T, H) or self.lse.dtype != torch.float32 or not self.lse.is_contiguous():
+            raise ValueError("out must be a contiguous [T, H, 512] tensor and lse a contiguous float32 [T, H]")
+        out_dtype = self.out.dtype
         self.workspace = torch.empty(max(workspace_bytes(self.p), 256), dtype=torch.uint8, device=q.device)
         self._keep = (q, kv_cache, block_table, seq_lens, qo_indptr, q_scale, kv_scale, sinks, bt_indptr)
         self._fn = lib().mla_decode

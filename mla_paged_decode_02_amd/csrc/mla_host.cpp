@@ -428,6 +428,38 @@ int mla_merge_segments(const float* segm_output, const float* segm_max, const fl
   return MLA_OK;
 }
 
+int mla_combine_lse(const void* shard_out, int32_t in_dtype, const float* shard_lse, int32_t num_shards,
+                    int32_t num_tokens, int32_t num_heads, const float* sinks, void* out, int32_t out_dtype,
+                    float* lse, void* stream) {
+  if (num_shards < 1 || num_shards > 64) return fail(MLA_ERR_INVALID_ARG, "num_shards %d out of [1, 64]", num_shards);
+  if (num_tokens < 0) return fail(MLA_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return fail(num_heads < 1 ? MLA_ERR_INVALID_ARG : MLA_ERR_UNSUPPORTED, "num_heads %d out of [1, 128]",
+                num_heads);
+  const int ic = out_code(in_dtype), oc = out_code(out_dtype);
+  if (ic < 0) return fail(MLA_ERR_UNSUPPORTED, "in_dtype %d not supported (bf16, fp16, fp32)", in_dtype);
+  if (oc < 0) return fail(MLA_ERR_UNSUPPORTED, "out_dtype %d not supported (bf16, fp16, fp32)", out_dtype);
+  if (num_tokens == 0) return MLA_OK;
+  if (!shard_out || !shard_lse || !out || !lse) return fail(MLA_ERR_INVALID_ARG, "combine buffers must not be NULL");
+  if (!aligned16(shard_out) || !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "shard_out and out must be 16-byte aligned");
+  mla::CombineLaunch c;
+  memset(&c, 0, sizeof(c));
+  c.shard_out = shard_out;
+  c.shard_lse = shard_lse;
+  c.in_dtype = ic;
+  c.num_shards = num_shards;
+  c.num_tokens = num_tokens;
+  c.num_heads = num_heads;
+  c.sinks = sinks;
+  c.out = out;
+  c.out_dtype = oc;
+  c.lse = lse;
+  hipError_t e = mla::launch_combine(c, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return MLA_OK;
+}
+
 namespace {
 
 // Both stages of the fused decode; stage 1 = the key stream, stage 2 = the

@@ -95,6 +95,17 @@ struct MergeLaunch {
   int32_t rows_wg, tt, grid_wgs;
 };
 
+struct CombineLaunch {
+  const void* shard_out;  // [W, T, H, 512]
+  const float* shard_lse; // [W, T, H]
+  int32_t in_dtype;       // 0 bf16, 1 fp16, 2 fp32
+  int32_t num_shards, num_tokens, num_heads;
+  const float* sinks;     // nullable
+  void* out;
+  int32_t out_dtype;
+  float* lse;
+};
+
 // Kernel shape chosen by the host for a decode batch.
 struct SegmentShape {
   bool fp8;
@@ -120,5 +131,6 @@ SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile);
 // segment kernel on (num_segments, num_reqs, chunks).
 hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
+hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream);
 
 }  // namespace mla

@@ -1359,6 +1359,90 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
   if (lane == 0) p.lse[row] = lse;
 }
 
+// ---------------------------------------------------------------------------
+// Cross-shard combine (decode context parallelism)
+// ---------------------------------------------------------------------------
+// One wave per (token, head) row; lane w < W holds shard w's LSE, and lane l
+// covers dims [8 l, 8 l + 8) of the output.  Natural-log weights
+// e^(lse_w - lse) on the shard outputs, then the sink once per row.
+template <int IN, int OUT>  // 0 bf16, 1 fp16, 2 fp32
+__global__ __launch_bounds__(256) void combine_kernel(CombineLaunch p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)p.num_tokens * p.num_heads;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int h = (int)(row % p.num_heads);
+  const int W = p.num_shards;
+  const float lw = lane < W ? p.shard_lse[(int64_t)lane * rows + row] : -INFINITY;
+  const bool nan_seen = __ballot(lw != lw) != 0;
+  float M = lw;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const bool has = M > -INFINITY;
+  const float wgt = (has && lw > -INFINITY) ? expf(lw - M) : 0.f;
+  float S = wgt;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) S += __shfl_xor(S, o);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < W; ++w) {
+    const float ww = __shfl(wgt, w);
+    if (ww == 0.f) continue;  // uniform: an empty shard adds nothing
+    const int64_t base = ((int64_t)w * rows + row) * kKvRank + 8 * lane;
+    float v[8];
+    if constexpr (IN == 2) {
+      const f32x4 a = *(const f32x4*)((const float*)p.shard_out + base);
+      const f32x4 b = *(const f32x4*)((const float*)p.shard_out + base + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+    } else {
+      const u32x4 u = *(const u32x4*)((const unsigned short*)p.shard_out + base);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned short lo = (unsigned short)(u[i] & 0xffff), hi = (unsigned short)(u[i] >> 16);
+        if constexpr (IN == 0) {
+          v[2 * i] = __uint_as_float((unsigned)lo << 16);
+          v[2 * i + 1] = __uint_as_float((unsigned)hi << 16);
+        } else {
+          v[2 * i] = (float)__builtin_bit_cast(_Float16, lo);
+          v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, hi);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += ww * v[i];
+  }
+  float lse = has ? M + logf(S) : -INFINITY;
+  float scale = has ? 1.0f / S : 0.f;
+  if (p.sinks) {
+    const float nl = logaddexp_f(lse, p.sinks[h]);
+    scale = has ? scale * expf(lse - nl) : 0.f;
+    lse = nl;
+  }
+  if (nan_seen) { lse = __builtin_nanf(""); scale = __builtin_nanf(""); }
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = has ? acc[i] * scale : (nan_seen ? scale : 0.f);
+  const int64_t orow = row * kKvRank + 8 * lane;
+  if constexpr (OUT == 2) {
+    f32x4* dst = (f32x4*)((float*)p.out + orow);
+    dst[0] = f32x4{o[0], o[1], o[2], o[3]};
+    dst[1] = f32x4{o[4], o[5], o[6], o[7]};
+  } else {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (OUT == 0) {
+        v[i] = (unsigned)f32_to_bf16_rne(o[2 * i]) | ((unsigned)f32_to_bf16_rne(o[2 * i + 1]) << 16);
+      } else {
+        const _Float16 a = (_Float16)o[2 * i], b = (_Float16)o[2 * i + 1];
+        v[i] = (unsigned)__builtin_bit_cast(unsigned short, a) | ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+      }
+    }
+    *(u32x4*)((unsigned short*)p.out + orow) = v;
+  }
+  if (lane == 0) p.lse[row] = lse;
+}
+
 template <bool FP8, int NW, int RG, bool CONTIG, bool WS>
 hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
   constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG, WS);
@@ -1441,6 +1525,26 @@ void launch_merge_t(const MergeLaunch& a, dim3 grid, hipStream_t stream) {
     case 1: hipLaunchKernelGGL((merge_kernel<1, SPLIT>), grid, dim3(256), 0, stream, a); break;
     default: hipLaunchKernelGGL((merge_kernel<2, SPLIT>), grid, dim3(256), 0, stream, a); break;
   }
+}
+
+template <int IN>
+void launch_combine_t(const CombineLaunch& a, dim3 grid, hipStream_t stream) {
+  switch (a.out_dtype) {
+    case 0: hipLaunchKernelGGL((combine_kernel<IN, 0>), grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((combine_kernel<IN, 1>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((combine_kernel<IN, 2>), grid, dim3(256), 0, stream, a); break;
+  }
+}
+
+hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.num_tokens * a.num_heads;
+  dim3 grid((unsigned)((rows + 3) / 4));
+  switch (a.in_dtype) {
+    case 0: launch_combine_t<0>(a, grid, stream); break;
+    case 1: launch_combine_t<1>(a, grid, stream); break;
+    default: launch_combine_t<2>(a, grid, stream); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {

@@ -401,6 +401,55 @@ def mla_decode_via_segments(w, num_segments: int, tile_size: int,
 
 
 # ---------------------------------------------------------------------------
+# Decode context parallelism: the LSE combine of key shards.
+# ---------------------------------------------------------------------------
+
+def combine_lse(shard_out: np.ndarray, shard_lse: np.ndarray,
+                sinks: Optional[np.ndarray] = None) -> tuple[np.ndarray, np.ndarray]:
+    """[backend page] DCP decode routing note (each rank attends over its
+    round-robin shard of the keys; partial outputs are merged across ranks by
+    LSE) and [merge page] module description (the natural-log LSE is what that
+    cross-rank merge consumes).
+
+    Shard w saw a disjoint subset of a row's keys and returned its softmax
+    output O_w and natural LSE_w = ln sum_{j in w} e^{s_j}.  Over the union:
+    LSE = ln sum_w e^{LSE_w} and O = sum_w O_w e^{LSE_w - LSE} (each O_w is
+    its shard's sum_j e^{s_j - LSE_w} V_j).  Shards with LSE_w = -inf hold no
+    key and add nothing.  The sink joins once, after the union, as in
+    ``attend``.  shard_out [W, T, H, 512], shard_lse [W, T, H].
+    """
+    so = np.asarray(shard_out, dtype=np.float64)
+    sl = np.asarray(shard_lse, dtype=np.float64)
+    W, T, H, D = so.shape
+    out = np.zeros((T, H, D))
+    lse = np.full((T, H), -np.inf)
+    for t in range(T):
+        for h in range(H):
+            ls = sl[:, t, h]
+            if np.isnan(ls).any():
+                out[t, h] = np.nan
+                lse[t, h] = np.nan
+                continue
+            fin = np.isfinite(ls)
+            if not fin.any():
+                continue
+            M = ls[fin].max()
+            total = M + math.log(sum(math.exp(x - M) for x in ls[fin]))
+            lse[t, h] = total
+            out[t, h] = sum(so[w, t, h] * math.exp(ls[w] - total) for w in range(W) if fin[w])
+    if sinks is not None:
+        sk = np.asarray(sinks, dtype=np.float64)
+        for t in range(T):
+            for h in range(H):
+                if np.isnan(lse[t, h]):
+                    continue
+                new = np.logaddexp(lse[t, h], sk[h])
+                out[t, h] *= math.exp(lse[t, h] - new) if np.isfinite(lse[t, h]) else 0.0
+                lse[t, h] = new
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
 # Byte accounting used to express throughput in the pages' unit.
 # ---------------------------------------------------------------------------
 

@@ -111,6 +111,25 @@ def _merge_sink_no_rescale(so, sm, se, part_lens, tile, sinks=None):
     return o, l
 
 
+_orig_combine = orc.combine_lse
+
+
+def _combine_base2(shard_out, shard_lse, sinks=None):
+    # shard weights as 2^(lse_w - lse) instead of e^(lse_w - lse)
+    return _orig_combine(shard_out, np.asarray(shard_lse) / math.log(2.0), sinks)
+
+
+def _combine_sink_per_shard(shard_out, shard_lse, sinks=None):
+    if sinks is None:
+        return _orig_combine(shard_out, shard_lse)
+    outs, lses = [], []
+    for w in range(np.asarray(shard_out).shape[0]):
+        o, l = _orig_combine(shard_out[w:w + 1], shard_lse[w:w + 1], sinks)
+        outs.append(o)
+        lses.append(l)
+    return _orig_combine(np.stack(outs), np.stack(lses))
+
+
 def _e4m3_bias8():
     def v(c):
         s = -1.0 if c & 0x80 else 1.0
@@ -141,6 +160,8 @@ MUTANTS = {
     "e4m3 exponent bias 8": ("_E4M3_TABLE", _e4m3_bias8()),
     "bf16 widened by 15 bits": ("decode_bf16", _bf16_shift15),
     "tile rule without the 128 cap": ("tile_size_for_block", lambda b: orc.largest_pow2_divisor(b)),
+    "shard combine weighs in base 2": ("combine_lse", _combine_base2),
+    "shard combine adds the sink on every shard": ("combine_lse", _combine_sink_per_shard),
 }
 
 # Cheapest pins first; a mutant only has to trip one of them.
@@ -161,6 +182,8 @@ PINS = [
     ("brute force bf16", lambda: P.test_oracle_matches_brute_force("bf16", False, False)),
     ("brute force causal sinks", lambda: P.test_oracle_matches_brute_force("bf16", True, True)),
     ("brute force fp8 causal", lambda: P.test_oracle_matches_brute_force("fp8_e4m3", True, False)),
+    ("combine closed forms", P.test_combine_lse_closed_forms),
+    ("dcp shards", lambda: P.test_dcp_shards_combine_to_the_direct_decode(2, True)),
 ]
 
 

@@ -468,3 +468,55 @@ def test_sparse_index_stream_is_attention_over_the_listed_rows():
         assert np.allclose(l[t], lse, atol=1e-12, rtol=0)
         assert np.allclose(o[t], p @ rows[:, :512], atol=1e-12, rtol=0)
     assert np.all(o[1] == 0) and np.allclose(l[1], w.sinks, atol=0)  # empty list: sink only
+
+
+# ------------------------------------------ decode context parallelism ----
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dcp_shards_combine_to_the_direct_decode(W, causal):
+    """Round-robin key shards, each decoded without sinks, then the LSE
+    combine with the sinks applied once, reproduce the direct decode of the
+    whole batch (plain route for qlen 1; the segmented route, one request per
+    verify token with its local causal window, for causal qlen > 1)."""
+    w = mi.make_workload(name="dcp", seq_lens=[37, 5, 64, 1, 0, 20], num_heads=3, block_size=8,
+                         dtype="bf16", qlens=[1, 3, 2, 1, 1, 4] if causal else None, causal=causal,
+                         sinks=True, seed=27)
+    ref_o, ref_l = orc.mla_decode(w)
+    shards = mi.dcp_shards(w, W)
+    outs, lses = [], []
+    for sw in shards:
+        assert sw.sinks is None
+        o, l = orc.mla_decode(sw)
+        outs.append(o)
+        lses.append(l)
+    o, l = orc.combine_lse(np.stack(outs), np.stack(lses), w.sinks)
+    assert np.allclose(o, ref_o, atol=1e-12, rtol=0)
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(fin, np.isfinite(l)) and np.allclose(l[fin], ref_l[fin], atol=1e-12, rtol=0)
+    # every key is on exactly one shard
+    total = sum(int(sw.seq_lens.sum()) for sw in shards)
+    if not causal:
+        assert total == int(w.seq_lens.sum())
+
+
+def test_combine_lse_closed_forms():
+    """Two shards with equal LSE average their outputs and add ln 2; a shard
+    with LSE -inf is ignored; a NaN LSE poisons only its row; no shard with a
+    key gives out 0 and LSE -inf, or the sink."""
+    rng = np.random.default_rng(3)
+    o = rng.standard_normal((2, 3, 2, 512))
+    l = np.array([[[0.5, -np.inf], [1.0, -np.inf], [np.nan, 2.0]],
+                  [[0.5, 3.0], [-np.inf, -np.inf], [0.0, 2.0]]])
+    out, lse = orc.combine_lse(o, l)
+    assert np.allclose(out[0, 0], (o[0, 0, 0] + o[1, 0, 0]) / 2, atol=1e-15)
+    assert abs(lse[0, 0] - (0.5 + math.log(2))) < 1e-15
+    assert np.array_equal(out[0, 1], o[1, 0, 1]) and lse[0, 1] == 3.0
+    assert np.array_equal(out[1, 0], o[0, 1, 0]) and lse[1, 0] == 1.0
+    assert np.all(out[1, 1] == 0) and lse[1, 1] == -np.inf
+    assert np.all(np.isnan(out[2, 0])) and np.isnan(lse[2, 0])
+    assert np.allclose(out[2, 1], (o[0, 2, 1] + o[1, 2, 1]) / 2, atol=1e-15)
+    sinks = np.array([0.25, -1.0])
+    out2, lse2 = orc.combine_lse(o, l, sinks)
+    assert np.all(out2[1, 1] == 0) and lse2[1, 1] == -1.0
+    assert abs(lse2[0, 0] - np.logaddexp(0.5 + math.log(2), 0.25)) < 1e-15
