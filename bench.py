@@ -38,6 +38,8 @@ WORKLOADS = {
     "bs52_ctx16k_h64_fp8_blk64": lambda mi: mi.bs52_fp8(64),
     "bs52_ctx16k_h128_bf16_blk256": lambda mi: mi.bs52_h128_bf16(),
     "ragged128_max32k_h96_fp8_causal_sinks": lambda mi: mi.ragged_h96_fp8(),
+    # the fused q prologue: bf16 q quantised to e4m3 in the q load
+    "bs52_ctx16k_h48_fp8_blk64_bf16q": lambda mi: mi.with_bf16_q(mi.bs52_fp8(48), seed=3),
     # index-stream (sparse top-k) decode: page size 1, per-token index lists
     "sparse_bs52_top2048_ctx16k_h16_bf16": lambda mi: mi.sparse_bs52(16, "bf16"),
     "sparse_bs52_top2048_ctx16k_h128_fp8": lambda mi: mi.sparse_bs52(128, "fp8_e4m3"),

@@ -80,7 +80,9 @@ typedef struct mla_problem {
   /* q: device [T, H, 576] of q_dtype.  Element strides; the last dim is
    * contiguous.  Base 16-byte aligned, strides multiples of 16 bytes. */
   const void* q;
-  int32_t q_dtype; /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3 (must equal kv_dtype) */
+  int32_t q_dtype; /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3: equal to kv_dtype, or
+                      BF16 with an FP8 cache (then q is quantised in the load path,
+                      see q_pe below) */
   int64_t q_stride_token;
   int64_t q_stride_head;
   const float* q_scale; /* device fp32 scalar: real q = code * q_scale; NULL = 1 */
@@ -130,6 +132,21 @@ typedef struct mla_problem {
    * ROCMAiterMLASparseImpl.forward_mqa / _forward_mla: one request per query
    * token, paged_kv_indptr / paged_kv_indices over a [rows, 1, 576] cache). */
   const int32_t* bt_indptr;
+
+  /* The q prologue of the sparse MLA page's forward_mqa (q arrives as the
+   * pair (ql_nope, q_pe); the fp8 path concatenates and quantises it with the
+   * layer's q scale before the decode), fused into the decode's q load:
+   *  - q_pe set: q holds the 512 latent dims [T, H, 512] (q strides, head
+   *    stride >= 512) and q_pe the 64 rope dims, device [T, H, 64] of q_dtype
+   *    with element strides q_pe_stride_token / q_pe_stride_head (last dim
+   *    contiguous, rows 16-byte aligned).  NULL: q is [T, H, 576].
+   *  - q_dtype BF16 with an FP8 cache: each q value x becomes the e4m3 code of
+   *    x / q_scale (IEEE single division, then saturated to +-448 and rounded
+   *    to nearest even), whose dequantised value code * q_scale enters the
+   *    scores; q_scale NULL = 1. */
+  const void* q_pe;
+  int64_t q_pe_stride_token;
+  int64_t q_pe_stride_head;
 } mla_problem;
 
 /*

@@ -339,6 +339,22 @@ def dcp_shards(w: Workload, num_shards: int) -> list:
     return shards
 
 
+def with_bf16_q(w: Workload, *, q_values: Optional[np.ndarray] = None, q_scale: Optional[float] = None,
+                seed: int = 0) -> Workload:
+    """The batch with its q handed over in bf16 while the cache stays fp8 (the
+    q the MLA layer produces before its fp8 quantisation).  Values ~N(0,1) by
+    default; the q scale defaults to amax / 448 (a static per-tensor scale)."""
+    assert w.kv_dtype == "fp8_e4m3"
+    if q_values is None:
+        q_values = torch.randn(w.q.shape, generator=_gen(seed + 313), dtype=torch.float32).numpy()
+    qt = torch.from_numpy(np.ascontiguousarray(q_values, dtype=np.float32))
+    codes = qt.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if q_scale is None:
+        amax = float(qt.abs().max()) if qt.numel() else 1.0
+        q_scale = float(np.float32(amax / FP8_E4M3_MAX)) if amax > 0 else 1.0
+    return replace(w, q=codes, q_dtype="bf16", q_scale=q_scale, name=w.name + "-bf16q")
+
+
 def tiny() -> Workload:
     """2 requests, lengths {100, 257}, 16 heads, bf16, page = TILE = 16, S = 4."""
     return make_workload(name="tiny", seq_lens=[100, 257], num_heads=16, block_size=16,

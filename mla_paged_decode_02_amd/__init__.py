@@ -79,6 +79,9 @@ class MlaProblem(ctypes.Structure):
         ("num_segments", ctypes.c_int32),
         ("max_workgroups", ctypes.c_int32),
         ("bt_indptr", ctypes.c_void_p),
+        ("q_pe", ctypes.c_void_p),
+        ("q_pe_stride_token", ctypes.c_int64),
+        ("q_pe_stride_head", ctypes.c_int64),
     ]
 
 
@@ -205,21 +208,30 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
                  causal: bool = False, q_scale: Optional[torch.Tensor] = None,
                  kv_scale: Optional[torch.Tensor] = None, tile_size: int = 0,
                  num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0,
-                 bt_indptr: Optional[torch.Tensor] = None) -> MlaProblem:
+                 bt_indptr: Optional[torch.Tensor] = None, q_pe: Optional[torch.Tensor] = None) -> MlaProblem:
     """Fill an ``mla_problem`` from tensors.  Host ints (max_seq_len, max_qlen)
     are passed by the caller so nothing is read back from the device.
 
     With ``bt_indptr`` (int32 [R+1]) the block table is one flat int32 list and
     request r's pages are ``block_table[bt_indptr[r]:bt_indptr[r+1]]``; with
-    block_size 1 that is a per-token index stream (sparse decode)."""
-    if q.ndim != 3 or q.shape[-1] != HEAD_DIM or q.stride(-1) != 1:
-        raise ValueError(f"q must be [T, H, 576] with a contiguous last dim, got {tuple(q.shape)}")
+    block_size 1 that is a per-token index stream (sparse decode).
+
+    With ``q_pe`` ([T, H, 64]) q holds only the 512 latent dims ([T, H, 512]):
+    the (ql_nope, q_pe) pair of the MLA layer, concatenated in the q load.  A
+    bf16 q with an fp8 cache is quantised in the q load with ``q_scale``."""
+    width = KV_LORA_RANK if q_pe is not None else HEAD_DIM
+    if q.ndim != 3 or q.shape[-1] != width or q.stride(-1) != 1:
+        raise ValueError(f"q must be [T, H, {width}] with a contiguous last dim, got {tuple(q.shape)}")
+    if q_pe is not None and (q_pe.ndim != 3 or tuple(q_pe.shape) != (q.shape[0], q.shape[1], HEAD_DIM - KV_LORA_RANK)
+                             or q_pe.stride(-1) != 1 or q_pe.dtype != q.dtype):
+        raise ValueError(f"q_pe must be [T, H, 64] of q's dtype with a contiguous last dim, got "
+                         f"{tuple(q_pe.shape)} {q_pe.dtype}")
     if kv_cache.ndim != 3 or kv_cache.shape[-1] != HEAD_DIM or not kv_cache.is_contiguous():
         raise ValueError(f"kv_cache must be a contiguous [blocks, page, 576] tensor, got {tuple(kv_cache.shape)}")
     qd, kd = _dtype_code(q, "q"), _dtype_code(kv_cache, "kv_cache")
-    if qd != kd:
+    if qd != kd and not (qd == MLA_DTYPE_BF16 and kd == MLA_DTYPE_FP8_E4M3):
         raise ValueError(f"q dtype {q.dtype} and kv_cache dtype {kv_cache.dtype} must match "
-                         "(bf16 with bf16, fp8 with fp8)")
+                         "(bf16 with bf16, fp8 with fp8; a bf16 q with an fp8 cache is quantised in the q load)")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
     if bt_indptr is not None:
@@ -242,6 +254,9 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
     p.q, p.q_dtype = _ptr(q), qd
     p.q_stride_token, p.q_stride_head = q.stride(0), q.stride(1)
     p.q_scale = _ptr(q_scale)
+    if q_pe is not None:
+        p.q_pe = _ptr(q_pe)
+        p.q_pe_stride_token, p.q_pe_stride_head = q_pe.stride(0), q_pe.stride(1)
     p.kv_cache, p.kv_dtype = _ptr(kv_cache), kd
     p.block_size, p.num_blocks = kv_cache.shape[1], kv_cache.shape[0]
     p.kv_scale = _ptr(kv_scale)
@@ -293,13 +308,13 @@ def workspace_bytes(p: MlaProblem) -> int:
 def decode_segments(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, num_segments: int,
                     max_seq_len: int, qo_indptr=None, max_qlen=None, causal=False, q_scale=None,
                     kv_scale=None, tile_size: int = 0, sum_seq_lens: int = 0, segm_output=None,
-                    segm_max=None, segm_expsum=None, bt_indptr=None, stream=None):
+                    segm_max=None, segm_expsum=None, bt_indptr=None, q_pe=None, stream=None):
     """Base-2 partials [T, H, S, 512], [T, H, S], [T, H, S] (fp32).  Slots of
     segments that hold no position are left as allocated (uninitialised)."""
     p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                      max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen, causal=causal,
                      q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size, num_segments=num_segments,
-                     sum_seq_lens=sum_seq_lens, bt_indptr=bt_indptr)
+                     sum_seq_lens=sum_seq_lens, bt_indptr=bt_indptr, q_pe=q_pe)
     T, H, S = q.shape[0], q.shape[1], int(num_segments)
     dev = q.device
     if segm_output is None:
@@ -336,13 +351,14 @@ def merge_segments(segm_output, segm_max, segm_expsum, part_lens, tile_size: int
 def decode(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_len: int,
            qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
            tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0,
-           out_dtype=torch.bfloat16, out=None, lse=None, workspace=None, bt_indptr=None, stream=None):
+           out_dtype=torch.bfloat16, out=None, lse=None, workspace=None, bt_indptr=None, q_pe=None,
+           stream=None):
     """Fused decode: returns (out [T, H, 512], lse [T, H])."""
     p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                      max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen, causal=causal,
                      q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
                      num_segments=num_segments, sum_seq_lens=sum_seq_lens, max_workgroups=max_workgroups,
-                     bt_indptr=bt_indptr)
+                     bt_indptr=bt_indptr, q_pe=q_pe)
     T, H = q.shape[0], q.shape[1]
     check_sinks(sinks, H)
     if out is None:
@@ -391,12 +407,13 @@ class Decoder:
     def __init__(self, q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_len: int,
                  qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
                  tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0,
-                 max_workgroups: int = 0, out_dtype=torch.bfloat16, bt_indptr=None, out=None, lse=None):
+                 max_workgroups: int = 0, out_dtype=torch.bfloat16, bt_indptr=None, out=None, lse=None,
+                 q_pe=None):
         self.p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                               max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen,
                               causal=causal, q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
                               num_segments=num_segments, sum_seq_lens=sum_seq_lens,
-                              max_workgroups=max_workgroups, bt_indptr=bt_indptr)
+                              max_workgroups=max_workgroups, bt_indptr=bt_indptr, q_pe=q_pe)
         check_sinks(sinks, q.shape[1])
         # num_segments == 0 keeps the balanced split (split_workgroups > 0);
         # otherwise the segment partition with that S.
@@ -413,7 +430,7 @@ class Decoder:
             raise ValueError("out must be a contiguous [T, H, 512] tensor and lse a contiguous float32 [T, H]")
         out_dtype = self.out.dtype
         self.workspace = torch.empty(max(workspace_bytes(self.p), 256), dtype=torch.uint8, device=q.device)
-        self._keep = (q, kv_cache, block_table, seq_lens, qo_indptr, q_scale, kv_scale, sinks, bt_indptr)
+        self._keep = (q, kv_cache, block_table, seq_lens, qo_indptr, q_scale, kv_scale, sinks, bt_indptr, q_pe)
         self._fn = lib().mla_decode
         self._args = (ctypes.byref(self.p), _ptr(sinks), _ptr(self.out), _out_code(out_dtype), _ptr(self.lse),
                       _ptr(self.workspace), self.workspace.numel())

@@ -79,8 +79,9 @@ int validate(const mla_problem* p, bool require_segments) {
     return fail(MLA_ERR_UNSUPPORTED, "q dtype %d not supported (bf16 or fp8-e4m3)", p->q_dtype);
   if (p->kv_dtype != MLA_DTYPE_BF16 && p->kv_dtype != MLA_DTYPE_FP8_E4M3)
     return fail(MLA_ERR_UNSUPPORTED, "kv_cache dtype %d not supported (bf16 or fp8-e4m3)", p->kv_dtype);
-  if (p->q_dtype != p->kv_dtype)
-    return fail(MLA_ERR_UNSUPPORTED, "q dtype %d and kv_cache dtype %d must match", p->q_dtype, p->kv_dtype);
+  if (p->q_dtype != p->kv_dtype && !(p->q_dtype == MLA_DTYPE_BF16 && p->kv_dtype == MLA_DTYPE_FP8_E4M3))
+    return fail(MLA_ERR_UNSUPPORTED, "q dtype %d and kv_cache dtype %d must match (or bf16 q with an fp8 cache)",
+                p->q_dtype, p->kv_dtype);
   if (p->block_size < 1) return fail(MLA_ERR_INVALID_ARG, "block_size must be >= 1, got %d", p->block_size);
   if (p->num_blocks < 1) return fail(MLA_ERR_INVALID_ARG, "num_blocks must be >= 1");
   if ((int64_t)p->num_blocks * p->block_size >= ((int64_t)1 << 31))
@@ -124,11 +125,20 @@ int validate(const mla_problem* p, bool require_segments) {
   const int eb = elem_bytes(p->q_dtype);
   if (!aligned16(p->q) || !aligned16(p->kv_cache))
     return fail(MLA_ERR_INVALID_ARG, "q and kv_cache must be 16-byte aligned");
-  if (p->q_stride_head < MLA_HEAD_DIM || p->q_stride_token < 0 || (p->q_stride_head * eb) % 16 != 0 ||
+  const int q_width = p->q_pe ? MLA_KV_LORA_RANK : MLA_HEAD_DIM;
+  if (p->q_stride_head < q_width || p->q_stride_token < 0 || (p->q_stride_head * eb) % 16 != 0 ||
       (p->q_stride_token * eb) % 16 != 0)
     return fail(MLA_ERR_INVALID_ARG,
-                "q strides (token %lld, head %lld elements) must be >= 0 / >= 576 and multiples of 16 bytes",
-                (long long)p->q_stride_token, (long long)p->q_stride_head);
+                "q strides (token %lld, head %lld elements) must be >= 0 / >= %d and multiples of 16 bytes",
+                (long long)p->q_stride_token, (long long)p->q_stride_head, q_width);
+  if (p->q_pe) {
+    if (!aligned16(p->q_pe)) return fail(MLA_ERR_INVALID_ARG, "q_pe must be 16-byte aligned");
+    if (p->q_pe_stride_head < MLA_HEAD_DIM - MLA_KV_LORA_RANK || p->q_pe_stride_token < 0 ||
+        (p->q_pe_stride_head * eb) % 16 != 0 || (p->q_pe_stride_token * eb) % 16 != 0)
+      return fail(MLA_ERR_INVALID_ARG,
+                  "q_pe strides (token %lld, head %lld elements) must be >= 0 / >= 64 and multiples of 16 bytes",
+                  (long long)p->q_pe_stride_token, (long long)p->q_pe_stride_head);
+  }
   if (!p->bt_indptr) {
     if (p->max_blocks_per_req < 1) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_req must be >= 1");
     if (cdiv64(p->max_seq_len, p->block_size) > p->max_blocks_per_req)
@@ -243,6 +253,10 @@ mla::SegmentLaunch make_launch(const mla_problem* p, int tile, int S, float* so,
   a.q = p->q;
   a.q_stride_token = p->q_stride_token;
   a.q_stride_head = p->q_stride_head;
+  a.q_pe = p->q_pe;
+  a.q_pe_stride_token = p->q_pe_stride_token;
+  a.q_pe_stride_head = p->q_pe_stride_head;
+  a.q_bf16 = p->q_dtype == MLA_DTYPE_BF16 && p->kv_dtype == MLA_DTYPE_FP8_E4M3;
   a.q_scale = p->q_scale;
   a.kv = static_cast<const char*>(p->kv_cache);
   a.num_blocks = p->num_blocks;

@@ -50,6 +50,9 @@ struct SegmentLaunch {
   const void* q;
   int64_t q_stride_token, q_stride_head;  // elements
   const float* q_scale;                   // nullable
+  const void* q_pe;                       // nullable: rope dims in their own tensor
+  int64_t q_pe_stride_token, q_pe_stride_head;
+  int32_t q_bf16;                         // bf16 q with an fp8 cache: quantise on load
   // cache
   const char* kv;
   int64_t num_blocks;

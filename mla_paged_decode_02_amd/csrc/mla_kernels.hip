@@ -243,7 +243,7 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
 // fp8 always uses 32); OCC waves per SIMD the register allocation must allow
 // (2 caps a wave at 256 registers).  Every wave of the workgroup calls it with
 // the same piece (it holds workgroup barriers).
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, int KS = 1>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, int KS = 1, bool QB = false>
 __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
                                           char (*lds)[TileGeom<FP8, TT>::kTileBytes], unsigned lds_u32,
                                           int* phys_rows, const Piece& pc) {
@@ -320,24 +320,75 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   typedef bf16x8 QBf[FP8 ? 1 : RG][FP8 ? 1 : 18];
   typedef i32x8 QLat[FP8 ? RG : 1][4];
   typedef long QRope[FP8 ? RG : 1][2];
+  // q as one [T, H, 576] tensor, or as q_nope [T, H, 512] + q_pe [T, H, 64];
+  // bf16 q with an fp8 cache is quantised here (code = e4m3 RNE of
+  // sat(q / q_scale)), the q prologue of the sparse page's forward_mqa.
   auto load_q = [&](QBf& qop, QLat& qlat, QRope& qrope) {
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
-      const int64_t qoff = (int64_t)(t0 + ti[q]) * p.q_stride_token + (int64_t)hh[q] * p.q_stride_head;
+      const int64_t tok = t0 + ti[q];
+      const int64_t qoff = tok * p.q_stride_token + (int64_t)hh[q] * p.q_stride_head;
+      const int64_t poff = p.q_pe ? tok * p.q_pe_stride_token + (int64_t)hh[q] * p.q_pe_stride_head
+                                  : qoff + kKvRank;
       if constexpr (FP8) {
-        const uint8_t* qb = (const uint8_t*)p.q + qoff;
+        if constexpr (!QB) {
+          const uint8_t* qb = (const uint8_t*)p.q + qoff;
+          const uint8_t* qr = (const uint8_t*)(p.q_pe ? p.q_pe : p.q) + poff;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 lo = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g) : u32x4{0, 0, 0, 0};
-          const u32x4 hi = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g + 16) : u32x4{0, 0, 0, 0};
-          qlat[q][c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int c = 0; c < 4; ++c) {
+            const u32x4 lo = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g) : u32x4{0, 0, 0, 0};
+            const u32x4 hi = rok[q] ? *(const u32x4*)(qb + 128 * c + 32 * g + 16) : u32x4{0, 0, 0, 0};
+            qlat[q][c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c) qrope[q][c] = rok[q] ? *(const long*)(qr + 32 * c + 8 * g) : 0;
+        } else {
+          const unsigned short* qb = (const unsigned short*)p.q + qoff;
+          const unsigned short* qr = (const unsigned short*)(p.q_pe ? p.q_pe : p.q) + poff;
+          const float qs_div = p.q_scale ? *p.q_scale : 1.0f;
+          // 8 bf16 values -> 8 e4m3 codes (two dwords)
+          auto quant8 = [&](const unsigned short* src) -> u32x2 {
+            const u32x4 v = rok[q] ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
+            float f[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              f[2 * i] = __uint_as_float(v[i] << 16);
+              f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float y = __fdiv_rn(f[i], qs_div);
+              f[i] = y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
+            }
+            u32x2 r;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * k], f[4 * k + 1], 0, false);
+              w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * k + 2], f[4 * k + 3], w, true);
+              r[k] = (unsigned)w;
+            }
+            return r;
+          };
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            i32x8 x;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const u32x2 w = quant8(qb + 128 * c + 32 * g + 8 * k);
+              x[2 * k] = (int)w[0];
+              x[2 * k + 1] = (int)w[1];
+            }
+            qlat[q][c] = x;
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c) qrope[q][c] = __builtin_bit_cast(long, quant8(qr + 32 * c + 8 * g));
         }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) qrope[q][c] = rok[q] ? *(const long*)(qb + 512 + 32 * c + 8 * g) : 0;
       } else {
+        const __bf16* qb = (const __bf16*)p.q + qoff;
+        const __bf16* qr = (const __bf16*)(p.q_pe ? p.q_pe : p.q) + poff;
 #pragma unroll
         for (int c = 0; c < 18; ++c) {
-          const __bf16* qp = (const __bf16*)p.q + qoff + 32 * c + 8 * g;
+          const __bf16* qp = c < 16 ? qb + 32 * c + 8 * g : qr + 32 * (c - 16) + 8 * g;
           const u32x4 v = rok[q] ? *(const u32x4*)qp : u32x4{0, 0, 0, 0};
           qop[q][c] = __builtin_bit_cast(bf16x8, v);
         }
@@ -989,7 +1040,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
 // Segment kernel: one workgroup per (segment, request, row chunk); the key
 // partition is the segment formula of the merge page's module description
 // (span = cdiv(len, S * TILE) * TILE; segment s = [s * span, min((s+1) * span, len))).
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, bool QB>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void segment_kernel(
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][TileGeom<FP8, TT>::kTileBytes];
@@ -1015,7 +1066,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
   pc.r = r; pc.t0 = t0; pc.qlen = qlen; pc.L = L; pc.row0 = row0;
   pc.seg_start = seg_start; pc.seg_end = min(seg_start + span, L);
   pc.mode = kOutSegment; pc.s = s; pc.prow0 = 0; pc.phase = 0;
-  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
+  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS, 1, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
 }
 
 // Work units of request r for a workgroup shape of rows_wg rows and TT-token
@@ -1057,7 +1108,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // With KS > 1 k-split waves a workgroup's KS waves share each of its pieces
 // tile by tile (one row group) and combine their states at the piece's end,
 // so a workgroup covers KS times the units with the same number of pieces.
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, int KS>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, int KS, bool QB>
 __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void split_kernel(
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[KS * NBUF][TileGeom<FP8, TT>::kTileBytes];
@@ -1130,7 +1181,7 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
     pc.s = 0;
     pc.prow0 = ((int64_t)gw * 2 + (pos == s_g ? 0 : 1)) * kRowsWG;
     pc.phase = (int)((pos - s_g) % KS);
-    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS, KS>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
+    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS, KS, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
     pos += b - a;
   }
 }
@@ -1443,40 +1494,50 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineLaunch p) {
   if (lane == 0) p.lse[row] = lse;
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG, bool WS>
+template <bool FP8, int NW, int RG, bool CONTIG, bool WS, bool QB>
 hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
   constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG, WS);
   constexpr int kTT = kCfg.tt;
   constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
   constexpr int kRing = kCfg.ring / kTileBytes;
   dim3 grid(a.num_segments, a.num_reqs, chunks);
-  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS>), grid, dim3(64 * NW), 0,
+  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS, QB>), grid, dim3(64 * NW), 0,
                      stream, a);
   return hipGetLastError();
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG, bool WS, int KS>
+template <bool FP8, int NW, int RG, bool CONTIG, bool WS, int KS, bool QB>
 hipError_t launch_split(const SegmentLaunch& a, int grid_wgs, hipStream_t stream) {
   constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG, WS);
   constexpr int kTT = kCfg.tt;
   constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
   constexpr int kRing = kCfg.ring / kTileBytes;
-  hipLaunchKernelGGL((split_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS, KS>), dim3(grid_wgs),
+  hipLaunchKernelGGL((split_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS, KS, QB>), dim3(grid_wgs),
                      dim3(64 * NW * KS), 0, stream, a);
   return hipGetLastError();
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG, bool WS = false>
+template <bool FP8, int NW, int RG, bool CONTIG, bool WS = false, bool QB = false>
 hipError_t launch_any(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
-  if (split_wgs <= 0) return launch_seg<FP8, NW, RG, CONTIG, WS>(a, sh.chunks, stream);
+  if (split_wgs <= 0) return launch_seg<FP8, NW, RG, CONTIG, WS, QB>(a, sh.chunks, stream);
   if constexpr (NW == 1 && RG == 1 && CONTIG && !WS) {
-    if (sh.ks == kSplitKs) return launch_split<FP8, NW, RG, CONTIG, WS, kSplitKs>(a, split_wgs, stream);
+    if (sh.ks == kSplitKs) return launch_split<FP8, NW, RG, CONTIG, WS, kSplitKs, QB>(a, split_wgs, stream);
   }
-  return launch_split<FP8, NW, RG, CONTIG, WS, 1>(a, split_wgs, stream);
+  return launch_split<FP8, NW, RG, CONTIG, WS, 1, QB>(a, split_wgs, stream);
 }
 
-template <bool FP8, bool CONTIG>
+// QB: bf16 q quantised in the q load (fp8 cache); the specialised-wave shapes
+// are not built for it.
+template <bool FP8, bool CONTIG, bool QB = false>
 hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
+  if constexpr (QB) {
+    switch (sh.waves) {
+      case 1: return launch_any<FP8, 1, 1, CONTIG, false, true>(a, sh, split_wgs, stream);
+      case 2: return launch_any<FP8, 2, 1, CONTIG, false, true>(a, sh, split_wgs, stream);
+      case 4: return launch_any<FP8, 4, 1, CONTIG, false, true>(a, sh, split_wgs, stream);
+      default: return launch_any<FP8, 8, 1, CONTIG, false, true>(a, sh, split_wgs, stream);
+    }
+  }
   if (sh.ws) {
     return sh.waves == 4 ? launch_any<FP8, 4, 1, CONTIG, true>(a, sh, split_wgs, stream)
                          : launch_any<FP8, 8, 1, CONTIG, true>(a, sh, split_wgs, stream);
@@ -1511,6 +1572,9 @@ SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
 
 hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
   if (sh.fp8) {
+    if (a.q_bf16)
+      return sh.contig ? launch_seg_shape<true, true, true>(a, sh, split_wgs, stream)
+                       : launch_seg_shape<true, false, true>(a, sh, split_wgs, stream);
     return sh.contig ? launch_seg_shape<true, true>(a, sh, split_wgs, stream)
                      : launch_seg_shape<true, false>(a, sh, split_wgs, stream);
   }

@@ -37,11 +37,13 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 import numpy as np
+import torch
 
 HEAD_DIM = 576
 KV_LORA_RANK = 512
 LOG2E = 1.0 / math.log(2.0)  # log2(e)
 LOGE2 = math.log(2.0)  # ln(2): converts a base-2 LSE to natural log
+FP8_E4M3_MAX = 448.0  # largest finite OCP e4m3fn value
 
 
 # ---------------------------------------------------------------------------
@@ -91,6 +93,20 @@ def decode(codes: np.ndarray, dtype: str, scale: Optional[float]) -> np.ndarray:
     if scale is not None:
         v = v * float(scale)
     return v
+
+
+def quantize_e4m3(values: np.ndarray, scale: Optional[float]) -> np.ndarray:
+    """[sparse page] ``forward_mqa``, fp8 branch: the bf16 q (ql_nope || q_pe)
+    is quantised with the layer's q scale before the decode, and the scale
+    later dequantises it.  The page does not print the quantiser.  Reading:
+    divide by the scale in IEEE single precision, saturate at +-448, round to
+    the nearest e4m3 code (ties to even), which torch's float8_e4m3fn cast
+    does.  The code is an integer decision, so it is taken in the precision the
+    library's q load uses (single).  Returns uint8 codes."""
+    s = np.float32(1.0 if scale is None else scale)
+    y = np.asarray(values, dtype=np.float32) / s
+    y = np.where(np.isnan(y), y, np.clip(y, -FP8_E4M3_MAX, FP8_E4M3_MAX)).astype(np.float32)
+    return torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 # ---------------------------------------------------------------------------
@@ -257,7 +273,11 @@ def decode_workload(w, reqs: Optional[Sequence[int]] = None) -> DecodedBatch:
             pages = pages_of(np.asarray(w.block_table), w.bt_indptr, r)
             idx = np.array([cache_row_index(pages, j, bsz) for j in range(n)])
             kv_flat[idx] = decode(flat[idx], w.kv_dtype, w.kv_scale)
-    q = decode(np.asarray(w.q), w.q_dtype, w.q_scale)
+    if w.q_dtype == "bf16" and w.kv_dtype == "fp8_e4m3":
+        # bf16 q with an fp8 cache: quantised first (the fused q prologue)
+        q = decode(quantize_e4m3(decode_bf16(np.asarray(w.q)), w.q_scale), "fp8_e4m3", w.q_scale)
+    else:
+        q = decode(np.asarray(w.q), w.q_dtype, w.q_scale)
     return DecodedBatch(q=q, kv_flat=kv_flat, block_table=np.asarray(w.block_table),
                         bt_indptr=None if w.bt_indptr is None else np.asarray(w.bt_indptr),
                         seq_lens=np.asarray(w.seq_lens), qo_indptr=np.asarray(w.qo_indptr),

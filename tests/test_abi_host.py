@@ -166,11 +166,36 @@ def test_sink_contract_wording():
 
 
 def test_dtype_pair_mismatch_raises():
+    """fp8 q needs an fp8 cache; a bf16 q with an fp8 cache is the fused
+    quantising q load and is accepted."""
+    q8 = torch.zeros((1, 16, 576), dtype=torch.float8_e4m3fn)
+    kv16 = torch.zeros((2, 16, 576), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="must match"):
+        m.make_problem(q8, kv16, torch.zeros((1, 1), dtype=torch.int32), torch.ones(1, dtype=torch.int32),
+                       softmax_scale=0.1, max_seq_len=1)
     q = torch.zeros((1, 16, 576), dtype=torch.bfloat16)
     kv = torch.zeros((2, 16, 576), dtype=torch.float8_e4m3fn)
-    with pytest.raises(ValueError, match="must match"):
-        m.make_problem(q, kv, torch.zeros((1, 1), dtype=torch.int32), torch.ones(1, dtype=torch.int32),
-                       softmax_scale=0.1, max_seq_len=1)
+    p = m.make_problem(q, kv, torch.zeros((1, 1), dtype=torch.int32), torch.ones(1, dtype=torch.int32),
+                       softmax_scale=0.1, max_seq_len=1, num_segments=1)
+    assert _status(p) == m.MLA_OK
+
+
+def test_split_q_validates():
+    """(q_nope [T, H, 512], q_pe [T, H, 64]): shapes and strides are checked."""
+    qn = torch.zeros((2, 16, 512), dtype=torch.bfloat16)
+    qp = torch.zeros((2, 16, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((2, 16, 576), dtype=torch.bfloat16)
+    bt = torch.zeros((2, 1), dtype=torch.int32)
+    sl = torch.ones(2, dtype=torch.int32)
+    p = m.make_problem(qn, kv, bt, sl, softmax_scale=0.1, max_seq_len=1, num_segments=1, q_pe=qp)
+    assert _status(p) == m.MLA_OK and p.q_pe and p.q_pe_stride_head == 64
+    p.q_pe_stride_head = 32          # rows would overlap
+    assert _status(p) == m.MLA_ERR_INVALID_ARG
+    with pytest.raises(ValueError, match="q_pe"):
+        m.make_problem(qn, kv, bt, sl, softmax_scale=0.1, max_seq_len=1, q_pe=qp[:, :, :32])
+    with pytest.raises(ValueError, match="512"):
+        m.make_problem(torch.zeros((2, 16, 576), dtype=torch.bfloat16), kv, bt, sl, softmax_scale=0.1,
+                       max_seq_len=1, q_pe=qp)
 
 
 # ------------------------------------------------------ balanced split plan --

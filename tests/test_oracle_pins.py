@@ -520,3 +520,41 @@ def test_combine_lse_closed_forms():
     out2, lse2 = orc.combine_lse(o, l, sinks)
     assert np.all(out2[1, 1] == 0) and lse2[1, 1] == -1.0
     assert abs(lse2[0, 0] - np.logaddexp(0.5 + math.log(2), 0.25)) < 1e-15
+
+
+# ---------------------------------------------------------- q prologue ----
+
+def test_e4m3_quantiser_is_nearest_code_ties_to_even():
+    """The q quantiser (division in single precision, saturation, torch's
+    e4m3fn cast) picks the nearest code of the OCP table, ties to the even
+    code, on values drawn to hit ties, subnormals and saturation."""
+    table = orc._E4M3_TABLE
+    finite = [c for c in range(256) if np.isfinite(table[c])]
+    rng = np.random.default_rng(5)
+    exact = np.array([table[c] for c in finite])
+    mids = (np.sort(np.unique(exact))[1:] + np.sort(np.unique(exact))[:-1]) / 2   # exact ties
+    vals = np.concatenate([exact, mids, rng.standard_normal(2000) * 40, [600.0, -1e4, 2.0 ** -11]])
+    vals = vals.astype(np.float32).astype(np.float64)
+    codes = orc.quantize_e4m3(vals, 1.0)
+    for v, c in zip(vals, codes):
+        y = min(max(v, -448.0), 448.0)
+        d = np.abs(exact - y)
+        best = np.flatnonzero(d == d.min())
+        cands = [finite[i] for i in best]
+        if len(set(table[c2] for c2 in cands)) > 1:        # a tie between two values: even mantissa
+            cands = [c2 for c2 in cands if (c2 & 1) == 0]
+        assert table[c] in [table[c2] for c2 in cands], (v, c)
+    # the scale divides first: 3.0 / 2.0 = 1.5 is a code
+    assert table[orc.quantize_e4m3(np.array([3.0]), 2.0)[0]] == 1.5
+
+
+def test_bf16_q_with_fp8_cache_uses_the_quantised_q():
+    """A bf16 q with an fp8 cache decodes as the batch whose fp8 q holds the
+    quantised codes (same q scale)."""
+    w = mi.make_workload(name="qp", seq_lens=[40, 7], num_heads=2, block_size=16, dtype="fp8_e4m3", seed=28)
+    wb = mi.with_bf16_q(w, seed=1)
+    codes = orc.quantize_e4m3(orc.decode_bf16(wb.q), wb.q_scale)
+    w8 = mi.with_(w, q=codes, q_scale=wb.q_scale)
+    o1, l1 = orc.mla_decode(wb)
+    o2, l2 = orc.mla_decode(w8)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
