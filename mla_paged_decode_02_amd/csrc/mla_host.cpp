@@ -158,7 +158,7 @@ int plan_segments(int num_reqs, int max_seq_len, int64_t sum_seq_lens, int num_h
   const mla::SegmentShape sh = mla::segment_shape(kv_dtype == MLA_DTYPE_FP8_E4M3, num_heads,
                                                   max_qlen < 1 ? 1 : max_qlen, tile);
   // Workgroups a CU holds at once (the LDS ring decides).
-  const int per_cu = mla::wgs_per_cu(sh.fp8, sh.waves, sh.rows_per_wave, sh.ws);
+  const int per_cu = mla::wgs_per_cu(sh.fp8, sh.waves, sh.rows_per_wave);
   const int64_t slots = (int64_t)(num_cus > 0 ? num_cus : 256) * per_cu;
   const int64_t total = sum_seq_lens > 0 ? sum_seq_lens : (int64_t)num_reqs * max_seq_len;
   // Segments sized so the longest request's pieces match one slot's share of
@@ -185,8 +185,8 @@ SplitPlan plan_split(const mla_problem* p, int tile) {
   SplitPlan sp;
   const int max_qlen = p->qo_indptr ? p->max_qlen : 1;
   sp.sh = mla::segment_shape(p->kv_dtype == MLA_DTYPE_FP8_E4M3, p->num_heads, max_qlen, tile);
-  sp.rows_wg = 16 * (sp.sh.ws ? sp.sh.waves / 2 : sp.sh.waves) * sp.sh.rows_per_wave;
-  sp.tt = mla::tile_tokens(sp.sh.fp8, sp.sh.waves, sp.sh.rows_per_wave, sp.sh.ws);
+  sp.rows_wg = 16 * sp.sh.waves * sp.sh.rows_per_wave;
+  sp.tt = mla::tile_tokens(sp.sh.fp8, sp.sh.waves, sp.sh.rows_per_wave);
   const int64_t chunks = cdiv64((int64_t)max_qlen * p->num_heads, sp.rows_wg);
   const int64_t max_units = (int64_t)p->num_reqs * chunks * cdiv64(p->max_seq_len > 0 ? p->max_seq_len : 1, sp.tt);
   if (max_units >= ((int64_t)1 << 31)) { sp.grid_wgs = 0; return sp; }
@@ -195,7 +195,7 @@ SplitPlan plan_split(const mla_problem* p, int tile) {
   const int64_t est = p->sum_seq_lens > 0 ? chunks * (cdiv64(p->sum_seq_lens, sp.tt) + p->num_reqs) : max_units;
   // (k-split waves: one workgroup holds ks waves' rings)
   const int64_t slots =
-      (int64_t)device_cus() * mla::wgs_per_cu(sp.sh.fp8, sp.sh.waves, sp.sh.rows_per_wave, sp.sh.ws) / sp.sh.ks;
+      (int64_t)device_cus() * mla::wgs_per_cu(sp.sh.fp8, sp.sh.waves, sp.sh.rows_per_wave) / sp.sh.ks;
   int64_t G = slots < est ? slots : est;
   // A batch of equal jobs (every request the same length and query count):
   // k workgroups per (request, row chunk) give every workgroup one piece.  A

@@ -22,27 +22,24 @@ struct ShapeCfg {
   int ring;
   int occ;
 };
-constexpr ShapeCfg shape_cfg(bool fp8, int waves, int rg, bool ws) {
+constexpr ShapeCfg shape_cfg(bool fp8, int waves, int rg) {
   // One wave: four workgroups per CU, one wave per SIMD, 2-slot ring.
   // Four waves: two workgroups per CU (two waves per SIMD hide each other's
   // LDS and MFMA latency; measured 1.9x faster than one 144 KiB workgroup).
   // Eight waves: one workgroup, two waves per SIMD.
   // Two row groups per wave: every LDS read feeds two MFMAs; one wave per SIMD.
-  // Specialised waves (S waves and P.V waves in pairs): one workgroup per CU,
-  // an 8-slot ring of 18 KiB tiles (fp8 32 tokens, bf16 16 tokens).
-  return ws ? ShapeCfg{fp8 ? 32 : 16, 147456, 2}
-       : rg == 2 ? (waves == 2 ? ShapeCfg{32, 73728, 1} : ShapeCfg{32, 147456, 1})
+  return rg == 2 ? (waves == 2 ? ShapeCfg{32, 73728, 1} : ShapeCfg{32, 147456, 1})
        : waves == 1 ? ShapeCfg{fp8 ? 32 : 16, 36864, 1}
        : waves == 2 ? ShapeCfg{32, 73728, 1}
        : waves == 4 ? ShapeCfg{fp8 ? 32 : 16, 73728, 2}
                     : ShapeCfg{fp8 ? 32 : 16, 147456, 2};
 }
-constexpr int tile_tokens(bool fp8, int waves, int rg, bool ws) { return shape_cfg(fp8, waves, rg, ws).tt; }
+constexpr int tile_tokens(bool fp8, int waves, int rg) { return shape_cfg(fp8, waves, rg).tt; }
 // Workgroups one CU holds at once: bound by LDS and by wave slots.
-constexpr int wgs_per_cu(bool fp8, int waves, int rg, bool ws) {
-  return (147456 / shape_cfg(fp8, waves, rg, ws).ring) < (4 * shape_cfg(fp8, waves, rg, ws).occ / waves)
-             ? (147456 / shape_cfg(fp8, waves, rg, ws).ring)
-             : (4 * shape_cfg(fp8, waves, rg, ws).occ / waves);
+constexpr int wgs_per_cu(bool fp8, int waves, int rg) {
+  return (147456 / shape_cfg(fp8, waves, rg).ring) < (4 * shape_cfg(fp8, waves, rg).occ / waves)
+             ? (147456 / shape_cfg(fp8, waves, rg).ring)
+             : (4 * shape_cfg(fp8, waves, rg).occ / waves);
 }
 
 struct SegmentLaunch {
@@ -114,7 +111,6 @@ struct SegmentShape {
   bool fp8;
   int waves;          // waves per workgroup (1, 2, 4 or 8)
   int rows_per_wave;  // 16-row groups per wave
-  bool ws;            // specialised waves: S waves and P.V waves in pairs (waves / 2 row groups)
   int chunks;         // row chunks per (request, segment)
   bool contig;        // TILE >= tile tokens: an LDS tile is one contiguous run of rows
   int ks;             // balanced split: k-split waves per workgroup (1 = none)
@@ -124,8 +120,8 @@ struct SegmentShape {
 // piece tile by tile and combine at its end, one workgroup per CU (the same
 // four waves per CU as four one-wave workgroups, a quarter of the pieces).
 constexpr int kSplitKs = 4;
-constexpr int split_ks(int waves, int rg, bool ws, bool contig) {
-  return (waves == 1 && rg == 1 && !ws && contig) ? kSplitKs : 1;
+constexpr int split_ks(int waves, int rg, bool contig) {
+  return (waves == 1 && rg == 1 && contig) ? kSplitKs : 1;
 }
 
 SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile);

@@ -243,7 +243,7 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
 // fp8 always uses 32); OCC waves per SIMD the register allocation must allow
 // (2 caps a wave at 256 registers).  Every wave of the workgroup calls it with
 // the same piece (it holds workgroup barriers).
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, int KS = 1, bool QB = false>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, int KS = 1, bool QB = false>
 __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
                                           char (*lds)[TileGeom<FP8, TT>::kTileBytes], unsigned lds_u32,
                                           int* phys_rows, const Piece& pc) {
@@ -257,19 +257,14 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   constexpr int kNIV = TT / kRowsPerV;                 // V-region DMA instructions
   constexpr int kNI = kTileBytes / 1024;               // all DMA instructions per tile
   constexpr int kNIw = kNIV / NW + (kNI - kNIV) / NW;   // per wave, lower bound
-  // WS: the workgroup's waves come in pairs over one 16-row group: wave g < NG
-  // computes S = K.Q^T and the softmax of the group's rows, wave NG + g
-  // accumulates their P.V (see the specialised loop below).
-  constexpr int NG = WS ? NW / 2 : NW;                  // row groups
-  constexpr int kRowsWG = 16 * RG * NG;
-  static_assert(!WS || (RG == 1 && NW % 2 == 0), "specialised waves: pairs of one row group");
+  constexpr int kRowsWG = 16 * RG * NW;
   static_assert(kTileBytes % 1024 == 0, "tile must be whole DMA instructions");
 
   const int lane = threadIdx.x & 63;
   // k-split waves (KS > 1) all take the one row group: their wave index
   // (kw below) picks tiles, not rows.
   const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int rgw = WS ? wave % NG : wave;                             // this wave's row group
+  const int rgw = wave;                                              // this wave's row group
   const int g = lane >> 4;
   const int n = lane & 15;
 
@@ -820,7 +815,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     }
   };
 
-  if constexpr (!WS) {
+  {
     // ---- every wave: QK, softmax and P.V of its own rows, tile after tile ----
     // k-split waves (KS > 1): wave kw takes tiles first, first + KS, ... of
     // the piece in its own ring slots kw * NBUF ..; pc.phase rotates the
@@ -937,115 +932,18 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       write_result(comb, lt, mf, bad, kDB * kw, kw == 0);
       __syncthreads();  // every wave is done with the others' slots
     }
-  } else {
-    // ---- specialised waves ----
-    // Iteration k (k = -1 .. ntiles-1): the S wave of a row group computes
-    // S = K.Q^T and the softmax of tile k+1 and leaves P^T (8 bytes a lane)
-    // and the rescale factors in LDS slot (k+1) % 2; its partner P.V wave
-    // takes P^T of tile k from slot k % 2, rescales its accumulator and
-    // accumulates V^T.P^T of tile k.  One barrier per iteration orders both,
-    // and every wave runs the same barrier sequence.  Tile j sits in ring slot
-    // j % NBUF; iteration k refills the slot of tile k - 1 (done with), so
-    // tiles k+2 .. k+NBUF-2 stay in flight while k and k+1 are in use.
-    static_assert(FP8 ? (kNB == 2) : (kNB == 1), "specialised waves: 8-byte P^T operands");
-    static_assert(KS == 1, "specialised waves take whole tiles");
-    __shared__ long ws_p[2][NG][64];
-    __shared__ float ws_alpha[2][NG][16];
-    __shared__ int ws_flag[2][NG];
-    __shared__ float ws_fin[NG][3][16];
-    const bool s_wave = wave < NG;
-
-#pragma unroll
-    for (int k = 0; k < NBUF - 2; ++k)
-      if (k < ntiles) issue_tile(k, k);
-
-    if (s_wave) {
-      QBf qop;
-      QLat qlat;
-      QRope qrope;
-      load_q(qop, qlat, qrope);
-      float m_run[RG], m_true[RG], l_run[RG];
-      m_run[0] = m_true[0] = -INFINITY;
-      l_run[0] = 0.f;
-      for (int k = -1; k < ntiles; ++k) {
-        if (k + 1 < ntiles) wait_tiles<kNIw, (NBUF >= 3 ? NBUF - 3 : 0)>(min(NBUF - 3, ntiles - 2 - k));
-        __syncthreads();
-        if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
-        if (k + 1 < ntiles && wave_has_rows) {
-          const int ps = (k + 1) & 1;
-          SBlk sblk;
-          qk_tile(lds[(k + 1) % NBUF], qop, qlat, qrope, sblk);
-          PVal pvv;
-          float alpha[RG];
-          const bool resc = softmax_tile(sblk, seg_start + (k + 1) * TT, m_run, m_true, l_run, pvv, alpha);
-          const bool any = __ballot(resc) != 0;
-          long word;
-          if constexpr (FP8) word = pvv.pb8[0];
-          else word = __builtin_bit_cast(long, pvv.pb[0]);
-          ws_p[ps][rgw][lane] = word;
-          if (g == 0) ws_alpha[ps][rgw][n] = alpha[0];
-          if (lane == 0) ws_flag[ps][rgw] = any ? 1 : 0;
-        }
-      }
-      // Final exact-max correction factor and the row sums, for the P.V wave.
-      const float f = (m_true[0] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[0] - m_true[0]);
-      float l_tot = l_run[0] + __shfl_xor(l_run[0], 16);
-      l_tot += __shfl_xor(l_tot, 32);
-      if (g == 0) {
-        ws_fin[rgw][0][n] = f;
-        ws_fin[rgw][1][n] = l_tot * f;
-        ws_fin[rgw][2][n] = m_true[0];
-      }
-      __syncthreads();
-      bad = __syncthreads_or(bad ? 1 : 0) != 0;
-    } else {
-      Acc acc;
-#pragma unroll
-      for (int d = 0; d < 32; ++d) acc[0][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int k = -1; k < ntiles; ++k) {
-        if (k + 1 < ntiles) wait_tiles<kNIw, (NBUF >= 3 ? NBUF - 3 : 0)>(min(NBUF - 3, ntiles - 2 - k));
-        __syncthreads();
-        if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
-        if (k >= 0 && wave_has_rows) {
-          const int ps = k & 1;
-          PVal pvv;
-          const long word = ws_p[ps][rgw][lane];
-          if constexpr (FP8) pvv.pb8[0] = word;
-          else pvv.pb[0] = __builtin_bit_cast(POp, word);
-          if (ws_flag[ps][rgw]) {
-            float alpha[RG];
-            alpha[0] = ws_alpha[ps][rgw][n];
-            rescale_acc(acc, alpha);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          pv_tile(lds[k % NBUF], acc, pvv);
-        }
-      }
-      __syncthreads();
-      const float f = ws_fin[rgw][0][n];
-      float l_tot[RG], m_fin[RG];
-      l_tot[0] = ws_fin[rgw][1][n];
-      m_fin[0] = ws_fin[rgw][2][n];
-#pragma unroll
-      for (int d = 0; d < 32; ++d) {
-        acc[0][d] *= f;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      bad = __syncthreads_or(bad ? 1 : 0) != 0;
-      write_result(acc, l_tot, m_fin, bad, 0, true);
-    }
   }
 }
 
 // Segment kernel: one workgroup per (segment, request, row chunk); the key
 // partition is the segment formula of the merge page's module description
 // (span = cdiv(len, S * TILE) * TILE; segment s = [s * span, min((s+1) * span, len))).
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, bool QB>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool QB>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void segment_kernel(
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][TileGeom<FP8, TT>::kTileBytes];
   __shared__ int phys_rows[CONTIG ? 1 : TT];
-  constexpr int kRowsWG = 16 * RG * (WS ? NW / 2 : NW);
+  constexpr int kRowsWG = 16 * RG * NW;
   const int s = blockIdx.x;
   const int r = blockIdx.y;
   const int chunk = blockIdx.z;
@@ -1066,7 +964,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
   pc.r = r; pc.t0 = t0; pc.qlen = qlen; pc.L = L; pc.row0 = row0;
   pc.seg_start = seg_start; pc.seg_end = min(seg_start + span, L);
   pc.mode = kOutSegment; pc.s = s; pc.prow0 = 0; pc.phase = 0;
-  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS, 1, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
+  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, 1, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
 }
 
 // Work units of request r for a workgroup shape of rows_wg rows and TT-token
@@ -1108,12 +1006,12 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // With KS > 1 k-split waves a workgroup's KS waves share each of its pieces
 // tile by tile (one row group) and combine their states at the piece's end,
 // so a workgroup covers KS times the units with the same number of pieces.
-template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool WS, int KS, bool QB>
+template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, int KS, bool QB>
 __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void split_kernel(
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[KS * NBUF][TileGeom<FP8, TT>::kTileBytes];
   __shared__ int phys_rows[CONTIG ? 1 : TT];
-  constexpr int kRowsWG = 16 * RG * (WS ? NW / 2 : NW);
+  constexpr int kRowsWG = 16 * RG * NW;
   const int lane = threadIdx.x & 63;
   const int R = p.num_reqs;
   const int G = gridDim.x;
@@ -1181,7 +1079,7 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
     pc.s = 0;
     pc.prow0 = ((int64_t)gw * 2 + (pos == s_g ? 0 : 1)) * kRowsWG;
     pc.phase = (int)((pos - s_g) % KS);
-    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, WS, KS, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
+    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, KS, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
     pos += b - a;
   }
 }
@@ -1494,59 +1392,46 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineLaunch p) {
   if (lane == 0) p.lse[row] = lse;
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG, bool WS, bool QB>
+template <bool FP8, int NW, int RG, bool CONTIG, bool QB>
 hipError_t launch_seg(const SegmentLaunch& a, int chunks, hipStream_t stream) {
-  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG, WS);
+  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG);
   constexpr int kTT = kCfg.tt;
   constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
   constexpr int kRing = kCfg.ring / kTileBytes;
   dim3 grid(a.num_segments, a.num_reqs, chunks);
-  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS, QB>), grid, dim3(64 * NW), 0,
+  hipLaunchKernelGGL((segment_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, QB>), grid, dim3(64 * NW), 0,
                      stream, a);
   return hipGetLastError();
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG, bool WS, int KS, bool QB>
+template <bool FP8, int NW, int RG, bool CONTIG, int KS, bool QB>
 hipError_t launch_split(const SegmentLaunch& a, int grid_wgs, hipStream_t stream) {
-  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG, WS);
+  constexpr ShapeCfg kCfg = shape_cfg(FP8, NW, RG);
   constexpr int kTT = kCfg.tt;
   constexpr int kTileBytes = kTT * (FP8 ? 576 : 1152);
   constexpr int kRing = kCfg.ring / kTileBytes;
-  hipLaunchKernelGGL((split_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, WS, KS, QB>), dim3(grid_wgs),
+  hipLaunchKernelGGL((split_kernel<FP8, NW, RG, kRing, CONTIG, kTT, kCfg.occ, KS, QB>), dim3(grid_wgs),
                      dim3(64 * NW * KS), 0, stream, a);
   return hipGetLastError();
 }
 
-template <bool FP8, int NW, int RG, bool CONTIG, bool WS = false, bool QB = false>
+template <bool FP8, int NW, int RG, bool CONTIG, bool QB = false>
 hipError_t launch_any(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
-  if (split_wgs <= 0) return launch_seg<FP8, NW, RG, CONTIG, WS, QB>(a, sh.chunks, stream);
-  if constexpr (NW == 1 && RG == 1 && CONTIG && !WS) {
-    if (sh.ks == kSplitKs) return launch_split<FP8, NW, RG, CONTIG, WS, kSplitKs, QB>(a, split_wgs, stream);
+  if (split_wgs <= 0) return launch_seg<FP8, NW, RG, CONTIG, QB>(a, sh.chunks, stream);
+  if constexpr (NW == 1 && RG == 1 && CONTIG) {
+    if (sh.ks == kSplitKs) return launch_split<FP8, NW, RG, CONTIG, kSplitKs, QB>(a, split_wgs, stream);
   }
-  return launch_split<FP8, NW, RG, CONTIG, WS, 1, QB>(a, split_wgs, stream);
+  return launch_split<FP8, NW, RG, CONTIG, 1, QB>(a, split_wgs, stream);
 }
 
-// QB: bf16 q quantised in the q load (fp8 cache); the specialised-wave shapes
-// are not built for it.
+// QB: bf16 q quantised in the q load (fp8 cache).
 template <bool FP8, bool CONTIG, bool QB = false>
 hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
-  if constexpr (QB) {
-    switch (sh.waves) {
-      case 1: return launch_any<FP8, 1, 1, CONTIG, false, true>(a, sh, split_wgs, stream);
-      case 2: return launch_any<FP8, 2, 1, CONTIG, false, true>(a, sh, split_wgs, stream);
-      case 4: return launch_any<FP8, 4, 1, CONTIG, false, true>(a, sh, split_wgs, stream);
-      default: return launch_any<FP8, 8, 1, CONTIG, false, true>(a, sh, split_wgs, stream);
-    }
-  }
-  if (sh.ws) {
-    return sh.waves == 4 ? launch_any<FP8, 4, 1, CONTIG, true>(a, sh, split_wgs, stream)
-                         : launch_any<FP8, 8, 1, CONTIG, true>(a, sh, split_wgs, stream);
-  }
   switch (sh.waves) {
-    case 1: return launch_any<FP8, 1, 1, CONTIG>(a, sh, split_wgs, stream);
-    case 2: return launch_any<FP8, 2, 1, CONTIG>(a, sh, split_wgs, stream);
-    case 4: return launch_any<FP8, 4, 1, CONTIG>(a, sh, split_wgs, stream);
-    default: return launch_any<FP8, 8, 1, CONTIG>(a, sh, split_wgs, stream);
+    case 1: return launch_any<FP8, 1, 1, CONTIG, QB>(a, sh, split_wgs, stream);
+    case 2: return launch_any<FP8, 2, 1, CONTIG, QB>(a, sh, split_wgs, stream);
+    case 4: return launch_any<FP8, 4, 1, CONTIG, QB>(a, sh, split_wgs, stream);
+    default: return launch_any<FP8, 8, 1, CONTIG, QB>(a, sh, split_wgs, stream);
   }
 }
 
@@ -1555,7 +1440,6 @@ hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, int 
 SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
   SegmentShape sh;
   sh.fp8 = fp8;
-  sh.ws = false;
   sh.rows_per_wave = 1;
   const int groups = (max_qlen * num_heads + 15) / 16;
   // groups of 16 rows -> waves per workgroup
@@ -1563,10 +1447,10 @@ SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
   else if (groups == 2) { sh.waves = 2; }
   else if (groups <= 4) { sh.waves = 4; }
   else                  { sh.waves = 8; }
-  const int rows_wg = 16 * sh.rows_per_wave * (sh.ws ? sh.waves / 2 : sh.waves);
+  const int rows_wg = 16 * sh.rows_per_wave * sh.waves;
   sh.chunks = (max_qlen * num_heads + rows_wg - 1) / rows_wg;
-  sh.contig = tile >= tile_tokens(fp8, sh.waves, sh.rows_per_wave, sh.ws);
-  sh.ks = split_ks(sh.waves, sh.rows_per_wave, sh.ws, sh.contig);
+  sh.contig = tile >= tile_tokens(fp8, sh.waves, sh.rows_per_wave);
+  sh.ks = split_ks(sh.waves, sh.rows_per_wave, sh.contig);
   return sh;
 }
 
