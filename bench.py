@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--extra", action="store_true", help="also time the other bs=52 workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-reqs", type=int, default=4)
+    ap.add_argument("--cpu-sample-reqs", type=int, default=0, help="requests the oracle times (0 = all)")
     ap.add_argument("--num-segments", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
@@ -311,27 +311,30 @@ def profiled_traffic(workload):
     return None
 
 
-def cpu_baseline(w, nreq):
-    """The fp64 oracle on `nreq` requests of the same batch, scaled to GB/s of
-    KV rows (the oracle as it stands, host cores)."""
-    import numpy as np
+def cpu_baseline(w, nreq, runs=3):
+    """The fp64 oracle on the first `nreq` requests of the same batch (all of
+    them by default), timed `runs` times; the median run, scaled to GB/s of KV
+    rows (the oracle as it stands, on the host cores)."""
     from oracle import mla_oracle as orc
 
-    reqs = list(range(min(nreq, w.num_reqs)))
-    t = time.perf_counter()
-    orc.mla_decode(w, reqs=reqs)
-    dt = time.perf_counter() - t
+    reqs = list(range(min(nreq, w.num_reqs) if nreq > 0 else w.num_reqs))
+    times = []
+    for _ in range(runs):
+        t = time.perf_counter()
+        orc.mla_decode(w, reqs=reqs)
+        times.append(time.perf_counter() - t)
+    dt = sorted(times)[len(times) // 2]
     esz = 2 if w.kv_dtype == "bf16" else 1
-    bytes_ = sum(int(w.seq_lens[r]) for r in reqs) * 576 * esz
+    rows = sum(int(w.seq_lens[r]) for r in reqs)
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s (effective KV)", "cores": cores,
+    return {"value": round(rows * 576 * esz / dt / 1e9, 4), "unit": "GB/s (effective KV)", "cores": cores,
             "kind": "oracle",
-            "sample": f"{len(reqs)} of {w.num_reqs} requests ({len(reqs) * int(w.seq_lens[0])} KV rows, "
-                      f"{w.num_heads} heads), fp64 NumPy oracle incl. page gather: {dt:.2f} s; "
-                      f"full step would take {dt * w.num_reqs / len(reqs):.1f} s"}
+            "sample": f"{len(reqs)} of {w.num_reqs} requests ({rows} KV rows, {w.num_heads} heads), fp64 NumPy "
+                      f"oracle incl. page gather; median of {runs} runs: {dt:.2f} s per run "
+                      f"({sum(times):.1f} s in all)"}
 
 
 def main():
