@@ -114,12 +114,16 @@ __device__ __forceinline__ void dma_lds16(i32x4 rsrc, unsigned lds_addr, int vof
 //   bf16: V region 32 x 1024 B, rope region 32 x 128 B at +32 KiB
 //   fp8 : V region 32 x  512 B, rope region 32 x  64 B at +16 KiB
 // 16-byte chunks are XOR-swizzled per row.  In the V region chunk c of row r
-// sits at c ^ swz_v(r), swz_v a permutation of 0..15 within each 16-row block
-// (((r & 7) << 1) | bit 3 of r), flipped in bit 0 for the second block, so
-// that (a) the 16 rows a K read touches, (b) the 8 rows x 2 chunks of a
-// 16-bit transpose read and (c) the 16 rows of an 8-bit transpose read each
-// hit distinct bank groups.  Rope chunks use swz_r(r) = (r >> 1) & 7 (bf16) or
-// (r >> 2) & 3 (fp8), distinct within each group of rows one read touches.
+// sits at c ^ swz_v(r), chosen so that the K reads (16 rows per 16-lane pass),
+// the 16-bit transpose reads (8 rows x 2 chunks) and the 8-bit transpose reads
+// (16 rows) meet no LDS bank conflict.  fp8 (512 B rows): (((r & 7) << 1) |
+// bit 3 of r), flipped in bit 0 for the second 16-row block.  bf16 (1024 B
+// rows): ((r & 7) << 1), flipped in bit 0 for the second block; rows r and
+// r + 8 share a chunk position there, which the LDS serves without conflict
+// (rows 8 KiB apart), while the fp8 pattern costs a second cycle per read at
+// this pitch (both measured with the LDS bank-conflict counter on gfx950).
+// Rope chunks use swz_r(r) = (r >> 1) & 7 (bf16) or (r >> 2) & 3 (fp8),
+// distinct within each group of rows one read touches.
 template <bool FP8>
 struct KvFmt;
 template <>
@@ -130,6 +134,7 @@ struct KvFmt<false> {  // bf16
   static constexpr int kVChunks = 64;
   static constexpr int kRopeChunks = 8;
   __device__ static int swz_r(int r) { return (r >> 1) & 7; }
+  __device__ static int swz_v(int r) { return ((r & 7) << 1) ^ ((r >> 4) & 1); }
 };
 template <>
 struct KvFmt<true> {  // fp8
@@ -139,9 +144,8 @@ struct KvFmt<true> {  // fp8
   static constexpr int kVChunks = 32;
   static constexpr int kRopeChunks = 4;
   __device__ static int swz_r(int r) { return (r >> 2) & 3; }
+  __device__ static int swz_v(int r) { return ((((r & 7) << 1) | ((r >> 3) & 1)) ^ ((r >> 4) & 1)); }
 };
-
-__device__ __forceinline__ int swz_v(int r) { return ((((r & 7) << 1) | ((r >> 3) & 1)) ^ ((r >> 4) & 1)); }
 
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));
@@ -434,13 +438,13 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         int voff, soff;
         if constexpr (!FP8) {
           soff = (vi < nvalid ? vi : 0) * kRowBytes;
-          voff = key16 ^ (16 * swz_v(vi));
+          voff = key16 ^ (16 * F::swz_v(vi));
         } else {
-          // rows 2vi (lanes 0-31) and 2vi+1 (lanes 32-63); swz_v(2vi+1) = swz_v(2vi) ^ 2
+          // rows 2vi (lanes 0-31) and 2vi+1 (lanes 32-63); F::swz_v(2vi+1) = F::swz_v(2vi) ^ 2
           const int row = 2 * vi + v_half;
           soff = 0;
           voff = (row < nvalid ? row * kRowBytes : 0) +
-                 ((16 * v_cpos) ^ (32 * v_half) ^ (16 * swz_v(2 * vi)));
+                 ((16 * v_cpos) ^ (32 * v_half) ^ (16 * F::swz_v(2 * vi)));
         }
         dma_lds16(rsrc, lbase + vi * 1024, voff, soff);
       }
@@ -476,10 +480,10 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         const int vi = wave + NW * i;
         const char* src;
         if constexpr (!FP8) {
-          src = row_ptr(vi) + (unsigned)(lane16 ^ (16 * swz_v(vi)));
+          src = row_ptr(vi) + (unsigned)(lane16 ^ (16 * F::swz_v(vi)));
         } else {
           const int row = 2 * vi + v_half;
-          src = row_ptr(row) + 16 * (v_cpos ^ swz_v(row));
+          src = row_ptr(row) + 16 * (v_cpos ^ F::swz_v(row));
         }
         __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(ldst + vi * 1024), 16, 0, 0);
       }
@@ -505,12 +509,12 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     kr_base[b] = kVRegion + lrow * F::kRopePitch;
     if constexpr (FP8) {
       // latent: logical chunks 8c + 2g (+1); rope: chunk 2c + g/2, half g & 1
-      kv_x[b] = (2 * g) ^ swz_v(lrow);
+      kv_x[b] = (2 * g) ^ F::swz_v(lrow);
       kr_x[b] = (g >> 1) ^ F::swz_r(lrow);
       kr_base[b] += 8 * (g & 1);
     } else {
       // logical chunk 4c + g
-      kv_x[b] = g ^ swz_v(lrow);
+      kv_x[b] = g ^ F::swz_v(lrow);
       kr_x[b] = g ^ F::swz_r(lrow);
     }
   }
@@ -521,7 +525,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     const int e = (lane >> 1) & 7, j = lane & 1;
     const int vrow = 16 * (e >> 2) + 4 * g + (e & 3);
     vt_base[0] = vrow * F::kVPitch + 8 * j;
-    vt_x[0] = swz_v(vrow);
+    vt_x[0] = F::swz_v(vrow);
     vt_base[1] = vt_x[1] = 0;
   } else {
     // address lane 16g + 4i + j: A-row 4g + i of block 0 / 1, dims 16db + 4j
@@ -530,7 +534,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     for (int rd = 0; rd < 2; ++rd) {
       const int vrow = 16 * rd + 4 * g + i4;
       vt_base[rd] = vrow * F::kVPitch + 8 * (j & 1);
-      vt_x[rd] = (j >> 1) ^ swz_v(vrow);
+      vt_x[rd] = (j >> 1) ^ F::swz_v(vrow);
     }
   }
 
