@@ -147,10 +147,16 @@ struct KvFmt<true> {  // fp8
   __device__ static int swz_v(int r) { return ((((r & 7) << 1) | ((r >> 3) & 1)) ^ ((r >> 4) & 1)); }
 };
 
+// Max over the four 16-lane rows of a wave (lanes n, n + 16, n + 32, n + 48).
+// gfx950's lane swaps run on the VALU: v_permlane32_swap pairs lanes l and
+// l ^ 32, v_permlane16_swap pairs lanes l and l ^ 16 (with both operands the
+// same value, the two results are the value and its partner's), so the
+// reduction needs no LDS round trip.
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const float (&p)[8]) {
