@@ -311,18 +311,20 @@ def profiled_traffic(workload):
     return None
 
 
-def cpu_baseline(w, nreq, runs=3):
+def cpu_baseline(w, nreq, min_runs=3, min_total_s=10.0, max_runs=15):
     """The fp64 oracle on the first `nreq` requests of the same batch (all of
-    them by default), timed `runs` times; the median run, scaled to GB/s of KV
-    rows (the oracle as it stands, on the host cores)."""
+    them by default), run at least `min_runs` times and until about
+    `min_total_s` seconds of CPU work are done; the median run, scaled to GB/s
+    of KV rows (the oracle as it stands, on the host cores)."""
     from oracle import mla_oracle as orc
 
     reqs = list(range(min(nreq, w.num_reqs) if nreq > 0 else w.num_reqs))
     times = []
-    for _ in range(runs):
+    while len(times) < min_runs or (sum(times) < min_total_s and len(times) < max_runs):
         t = time.perf_counter()
         orc.mla_decode(w, reqs=reqs)
         times.append(time.perf_counter() - t)
+    runs = len(times)
     dt = sorted(times)[len(times) // 2]
     esz = 2 if w.kv_dtype == "bf16" else 1
     rows = sum(int(w.seq_lens[r]) for r in reqs)
