@@ -576,10 +576,20 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     for (int q = 0; q < RG; ++q) sblk[q][0] = sblk[q][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (FP8) {
       // latent: 4 x (16x16x128 f8f6f4) per block; steps (c, b), c = 0..3
+      // (8 c) ^ x = 16 (c / 2) + (8 (c % 2)) ^ x for x < 16: two per-lane
+      // bases per block and half, the rest an immediate offset.
+      int kl2[kNB][2][2];
+#pragma unroll
+      for (int b = 0; b < kNB; ++b)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          kl2[b][e][0] = kvb[b] + 16 * ((8 * e) ^ kvx[b]);
+          kl2[b][e][1] = kvb[b] + 16 * ((8 * e) ^ (kvx[b] ^ 1));
+        }
       auto lat_load = [&](int st) -> i32x8 {
         const int c = st / kNB, b = st % kNB;
-        const u32x4 lo = lds_load<u32x4>(buf, kvb[b] + 16 * ((8 * c) ^ kvx[b]));
-        const u32x4 hi = lds_load<u32x4>(buf, kvb[b] + 16 * ((8 * c) ^ (kvx[b] ^ 1)));
+        const u32x4 lo = lds_load<u32x4>(buf, kl2[b][c & 1][0] + 256 * (c >> 1));
+        const u32x4 hi = lds_load<u32x4>(buf, kl2[b][c & 1][1] + 256 * (c >> 1));
         return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       constexpr int kLat = 4 * kNB;
@@ -611,9 +621,16 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     } else {
       // 18 * kNB (chunk, block) steps of 16x16x32 bf16
       constexpr int kSteps = 18 * kNB;
+      // (4 c) ^ kvx = 16 (c / 4) + (4 (c % 4)) ^ kvx for c < 16: four per-lane
+      // bases per block, the rest an immediate offset.
+      int kb4[kNB][4];
+#pragma unroll
+      for (int b = 0; b < kNB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kb4[b][e] = kvb[b] + 16 * ((4 * e) ^ kvx[b]);
       auto k_off = [&](int st) {
         const int c = st / kNB, b = st % kNB;
-        if (c < 16) return kvb[b] + 16 * ((4 * c) ^ kvx[b]);
+        if (c < 16) return kb4[b][c & 3] + 256 * (c >> 2);
         return krb[b] + 16 * ((4 * (c - 16)) ^ krx[b]);
       };
       bf16x8 kop[kPF];
@@ -705,15 +722,27 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     int vtb[2], vtx[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) { vtb[b] = opaque(vt_base[b]); vtx[b] = opaque(vt_x[b]); }
+    // The swizzle (vtx < 16) only touches the low four chunk bits, so the
+    // chunk splits into an immediate offset plus a per-lane part that repeats:
+    // with one 16-token block (2 db) ^ vtx = 16 (db / 8) + (2 (db % 8)) ^ vtx,
+    // for fp8 db ^ vtx = 16 (db / 16) + (db % 16) ^ vtx.  The per-lane bases
+    // are formed once per tile instead of an address per read.
+    const char* vb8[kNB == 1 ? 8 : 1];
+    const char* vb16[FP8 ? 16 : 1];
+    if constexpr (kNB == 1) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) vb8[d] = buf + vtb[0] + 16 * ((2 * d) ^ vtx[0]);
+    } else if constexpr (FP8) {
+#pragma unroll
+      for (int d = 0; d < 16; ++d) vb16[d] = buf + vtb[0] + 16 * (d ^ vtx[0]);
+    }
     auto v_load = [&](int db) -> VRaw {
       if constexpr (kNB == 1) {
         // one 16-token block: k-slots 4g..4g+3 from a single transpose read
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(buf + vtb[0] + 16 * ((2 * db) ^ vtx[0])));
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vb8[db & 7] + 256 * (db >> 3)));
       } else if constexpr (FP8) {
         // logical chunk db, half j
-        return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (LDS_AS i32x2*)(buf + vtb[0] + 16 * (db ^ vtx[0])));
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(vb16[db & 15] + 256 * (db >> 4)));
       } else {
         // logical chunk 2db + j/2, half j & 1
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
