@@ -313,6 +313,16 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     end_row[q] = min(seg_end, lim);
   }
   const bool wave_has_rows = row0 + rgw * RG * 16 < M;
+  // Keys every valid row of this wave's row group sees (and the piece
+  // streams): tiles below it need no mask.
+  int end_min[RG];
+#pragma unroll
+  for (int q = 0; q < RG; ++q) {
+    int v = rok[q] ? end_row[q] : 0x7fffffff;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = min(v, __shfl_xor(v, off));
+    end_min[q] = min(__builtin_amdgcn_readfirstlane(v), eff_end);
+  }
 
   const float qs = p.q_scale ? *p.q_scale : 1.0f;
   const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
@@ -420,50 +430,71 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   const int rope_row_in = lane / F::kRopeChunks;
   const int rope_cpos = lane % F::kRopeChunks;
 
+  // Contiguous tiles: a scalar cursor over the page table.  A wave issues its
+  // tiles in order, KS * TT keys apart, so the page index and the offset in
+  // the page advance by addition; the page number is reloaded only when the
+  // page changes.  A call for any other tile locates it by division.
+  int cur_start = -1, cur_blk_i = 0, cur_in = 0, cached_blk_i = -1;
+  int64_t cached_off = 0;  // byte offset of the cached page's first row
   auto issue_tile = [&](int k, int b) {
     const int tile_start = seg_start + k * TT;
     const int nvalid = min(TT, eff_end - tile_start);
     char* ldst = &lds[b][0];
     if constexpr (CONTIG) {
-      // Uniform address, read-only table: a scalar load through the constant
-      // address space, so no vector-memory wait drains the DMA stream.
-      const int blk_i = tile_start / p.block_size;
-      int blk = ((const __attribute__((address_space(4))) int*)p.block_table)
-          [bt_base + (int64_t)blk_i * p.bt_stride_col];
-      if (blk < 0 || blk >= p.num_blocks) { blk = 0; bad = true; }
-      const int64_t phys0 = (int64_t)blk * p.block_size + (tile_start - blk_i * p.block_size);
-      // Buffer descriptor over the tile's 32 rows (a guard: no offset below
+      if (tile_start != cur_start) {
+        cur_blk_i = tile_start / p.block_size;
+        cur_in = tile_start - cur_blk_i * p.block_size;
+      }
+      if (cur_blk_i != cached_blk_i) {
+        // Uniform address, read-only table: a scalar load through the constant
+        // address space, so no vector-memory wait drains the DMA stream.
+        int blk = ((const __attribute__((address_space(4))) int*)p.block_table)
+            [bt_base + (int64_t)cur_blk_i * p.bt_stride_col];
+        if (blk < 0 || blk >= p.num_blocks) { blk = 0; bad = true; }
+        cached_off = (int64_t)blk * p.block_size * kRowBytes;
+        cached_blk_i = cur_blk_i;
+      }
+      // Buffer descriptor over the tile's rows (a guard: no offset below
       // leaves them); per instruction a scalar row offset plus one 32-bit
       // per-lane chunk offset.
-      const i32x4 rsrc = make_rsrc(p.kv + phys0 * kRowBytes, TT * kRowBytes);
+      const i32x4 rsrc = make_rsrc(p.kv + cached_off + (int64_t)cur_in * kRowBytes, TT * kRowBytes);
       const unsigned lbase = lds_u32 + (unsigned)(b * kTileBytes);
       const int key16 = opaque(lane16);
+      // Rows at or past the valid count load tile row 0; a full tile needs
+      // no clamp.
+      auto dma_all = [&](auto full_tag) {
+        constexpr bool kFull = decltype(full_tag)::value;
+        auto clamp = [&](int row) { return kFull ? row : (row < nvalid ? row : 0); };
 #pragma unroll
-      for (int i = 0; i < kVPerWave; ++i) {
-        const int vi = wave + NW * i;
-        int voff, soff;
-        if constexpr (!FP8) {
-          soff = (vi < nvalid ? vi : 0) * kRowBytes;
-          voff = key16 ^ (16 * F::swz_v(vi));
-        } else {
-          // rows 2vi (lanes 0-31) and 2vi+1 (lanes 32-63); F::swz_v(2vi+1) = F::swz_v(2vi) ^ 2
-          const int row = 2 * vi + v_half;
-          soff = 0;
-          voff = (row < nvalid ? row * kRowBytes : 0) +
-                 ((16 * v_cpos) ^ (32 * v_half) ^ (16 * F::swz_v(2 * vi)));
+        for (int i = 0; i < kVPerWave; ++i) {
+          const int vi = wave + NW * i;
+          int voff, soff;
+          if constexpr (!FP8) {
+            soff = clamp(vi) * kRowBytes;
+            voff = key16 ^ (16 * F::swz_v(vi));
+          } else {
+            // rows 2vi (lanes 0-31) and 2vi+1 (lanes 32-63); F::swz_v(2vi+1) = F::swz_v(2vi) ^ 2
+            const int row = 2 * vi + v_half;
+            soff = 0;
+            voff = clamp(row) * kRowBytes + ((16 * v_cpos) ^ (32 * v_half) ^ (16 * F::swz_v(2 * vi)));
+          }
+          dma_lds16(rsrc, lbase + vi * 1024, voff, soff);
         }
-        dma_lds16(rsrc, lbase + vi * 1024, voff, soff);
-      }
 #pragma unroll
-      for (int i = 0; i < kRopePerWaveMax; ++i) {
-        const int ri = wave + NW * i;
-        if (ri < kNIR) {
-          const int row = ri * kRowsPerRope + rope_row_in;
-          const int rr = row < nvalid ? row : 0;
-          const int voff = rr * kRowBytes + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
-          dma_lds16(rsrc, lbase + (kNIV + ri) * 1024, voff, 0);
+        for (int i = 0; i < kRopePerWaveMax; ++i) {
+          const int ri = wave + NW * i;
+          if (ri < kNIR) {
+            const int row = ri * kRowsPerRope + rope_row_in;
+            const int voff = clamp(row) * kRowBytes + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
+            dma_lds16(rsrc, lbase + (kNIV + ri) * 1024, voff, 0);
+          }
         }
-      }
+      };
+      dma_all(std::false_type{});
+      // Advance the cursor to this wave's next tile.
+      cur_start = tile_start + KS * TT;
+      cur_in += KS * TT;
+      while (cur_in >= p.block_size) { cur_in -= p.block_size; ++cur_blk_i; }
     } else {
       // Rows of a tile span several pages: thread j < 32 resolves tile row j
       // (rows past the valid count resolve to tile row 0).
@@ -660,13 +691,21 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     for (int q = 0; q < RG; ++q) {
       float x[4 * kNB];
       float mloc = -INFINITY;
+      if (tile_start + TT <= end_min[q]) {
 #pragma unroll
-      for (int i = 0; i < 4 * kNB; ++i) {
-        // score slot i: block i/4, A-row 4g + i%4
-        const int tok = tile_start + 16 * (i >> 2) + 4 * g + (i & 3);
-        const float v = (tok < end_row[q]) ? sblk[q][i >> 2][i & 3] * sl2 : -INFINITY;
-        x[i] = v;
-        mloc = fmaxf(mloc, v);
+        for (int i = 0; i < 4 * kNB; ++i) {
+          x[i] = sblk[q][i >> 2][i & 3] * sl2;
+          mloc = fmaxf(mloc, x[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4 * kNB; ++i) {
+          // score slot i: block i/4, A-row 4g + i%4
+          const int tok = tile_start + 16 * (i >> 2) + 4 * g + (i & 3);
+          const float v = (tok < end_row[q]) ? sblk[q][i >> 2][i & 3] * sl2 : -INFINITY;
+          x[i] = v;
+          mloc = fmaxf(mloc, v);
+        }
       }
       mloc = wave_max(mloc);
       m_true[q] = fmaxf(m_true[q], mloc);
