@@ -150,6 +150,10 @@ SWEEP = [
     ("fp8_e4m3", 96, 64, [900, 44, 3000], [1, 4, 2], True, True, 3),
     ("fp8_e4m3", 128, 128, [1024, 3], None, False, False, 2),
     ("fp8_e4m3", 7, 8, [170, 33], [3, 1], True, True, 4),
+    # pages that are not a power of two: a k-split wave's next tile lies one or
+    # more pages on (48 < 4 waves x 16 keys, 96 < 4 waves x 32 keys)
+    ("bf16", 16, 48, [777, 100, 48], None, False, False, 3),
+    ("fp8_e4m3", 16, 96, [1000, 300, 97], None, False, True, 3),
 ]
 
 
