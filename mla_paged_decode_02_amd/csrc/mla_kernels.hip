@@ -108,6 +108,33 @@ __device__ __forceinline__ void dma_lds16(i32x4 rsrc, unsigned lds_addr, int vof
       : "memory", "m0");
 }
 
+// One 4-byte-per-lane load from a buffer straight into LDS (64 lanes fill
+// 256 B at lds_addr).  Tracked by the kernels' own vmcnt waits, like dma_lds16.
+__device__ __forceinline__ void dma_lds4(i32x4 rsrc, unsigned lds_addr, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc),
+        "s"(__builtin_amdgcn_readfirstlane(0))
+      : "memory", "m0");
+}
+
+// One 16-byte-per-lane load from a 64-bit address per lane straight into LDS
+// (64 lanes fill 1 KiB at lds_addr): the gather path's row loads, which may
+// lie anywhere in the cache.  Tracked by the kernels' own vmcnt waits.
+__device__ __forceinline__ void dma_lds16_gather(unsigned lds_addr, const void* src) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+      : "memory", "m0");
+}
+
+// Page-table entries a gathering workgroup keeps in LDS at a time.
+constexpr int kIdxCap = 256;
+
 // LDS tile layout (32 tokens).  The 512 latent dims (also V) and the 64 rope
 // dims of a row live in two regions so that one DMA instruction (64 lanes x
 // 16 B) covers whole rows:
@@ -256,7 +283,7 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
 template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, int KS = 1, bool QB = false>
 __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
                                           char (*lds)[TileGeom<FP8, TT>::kTileBytes], unsigned lds_u32,
-                                          int* phys_rows, const Piece& pc) {
+                                          int* phys_rows, int* idx_buf, const Piece& pc) {
   using F = KvFmt<FP8>;
   static_assert(TT == 32 || (TT == 16 && !FP8), "tile shape");
   constexpr int kNB = TT / 16;                         // 16-token blocks per tile
@@ -430,6 +457,26 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   const int rope_row_in = lane / F::kRopeChunks;
   const int rope_cpos = lane % F::kRopeChunks;
 
+  // Gathered tiles: a window of the request's page-table entries in LDS,
+  // starting at page idx_pg0.  Every wave calls load_idx at the same tile;
+  // it waits for all of the wave's loads (the window is refilled at most once
+  // per kIdxCap pages).  Entries past the table repeat its last one.
+  int idx_pg0 = 0x7fffffff / 2;
+  auto load_idx = [&](int pg) {
+    const int npages = max(cap / p.block_size, 1);
+    const int64_t stride = p.bt_stride_col;
+    const i32x4 trs = make_rsrc(p.block_table + bt_base,
+                                (int)min((int64_t)0x7fffffff, ((int64_t)(npages - 1) * stride + 1) * 4));
+    __syncthreads();  // every wave is done with the previous window
+    for (int i = wave; i < kIdxCap / 64; i += NW) {
+      const int e = min(pg + i * 64 + lane, npages - 1);
+      dma_lds4(trs, lds_address(idx_buf) + (unsigned)(i * 256), (int)((int64_t)e * stride * 4));
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    idx_pg0 = pg;
+  };
+
   // Contiguous tiles: a scalar cursor over the page table.  A wave issues its
   // tiles in order, KS * TT keys apart, so the page index and the offset in
   // the page advance by addition; the page number is reloaded only when the
@@ -439,7 +486,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   auto issue_tile = [&](int k, int b) {
     const int tile_start = seg_start + k * TT;
     const int nvalid = min(TT, eff_end - tile_start);
-    char* ldst = &lds[b][0];
+    const unsigned lbase = lds_u32 + (unsigned)(b * kTileBytes);
     if constexpr (CONTIG) {
       if (tile_start != cur_start) {
         cur_blk_i = tile_start / p.block_size;
@@ -458,7 +505,6 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       // leaves them); per instruction a scalar row offset plus one 32-bit
       // per-lane chunk offset.
       const i32x4 rsrc = make_rsrc(p.kv + cached_off + (int64_t)cur_in * kRowBytes, TT * kRowBytes);
-      const unsigned lbase = lds_u32 + (unsigned)(b * kTileBytes);
       const int key16 = opaque(lane16);
       // Rows at or past the valid count load tile row 0; a full tile needs
       // no clamp.
@@ -496,13 +542,19 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       cur_in += KS * TT;
       while (cur_in >= p.block_size) { cur_in -= p.block_size; ++cur_blk_i; }
     } else {
-      // Rows of a tile span several pages: thread j < 32 resolves tile row j
-      // (rows past the valid count resolve to tile row 0).
+      // Rows of a tile span several pages.  The page entries come from a
+      // window of kIdxCap table entries in LDS, refilled (one full wait) when
+      // a tile reaches past it, so no table load waits inside the stream.
+      const int pg_first = tile_start / p.block_size;
+      const int pg_last = (tile_start + max(nvalid, 1) - 1) / p.block_size;
+      if (pg_first < idx_pg0 || pg_last >= idx_pg0 + kIdxCap) load_idx(pg_first);
+      // Thread j < TT resolves tile row j (rows past the valid count resolve
+      // to tile row 0).
       __syncthreads();  // previous readers of phys_rows are done
       if (threadIdx.x < TT) {
         const int j = tile_start + ((int)threadIdx.x < nvalid ? (int)threadIdx.x : 0);
         const int blk_i = j / p.block_size;
-        const int blk = p.block_table[bt_base + (int64_t)blk_i * p.bt_stride_col];
+        const int blk = idx_buf[blk_i - idx_pg0];
         phys_rows[threadIdx.x] =
             (blk < 0 || blk >= p.num_blocks) ? -1 : blk * p.block_size + (j - blk_i * p.block_size);
       }
@@ -522,7 +574,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
           const int row = 2 * vi + v_half;
           src = row_ptr(row) + 16 * (v_cpos ^ F::swz_v(row));
         }
-        __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(ldst + vi * 1024), 16, 0, 0);
+        dma_lds16_gather(lbase + vi * 1024, src);
       }
 #pragma unroll
       for (int i = 0; i < kRopePerWaveMax; ++i) {
@@ -530,7 +582,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         if (ri < kNIR) {
           const int row = ri * kRowsPerRope + rope_row_in;
           const char* src = row_ptr(row) + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
-          __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(ldst + (kNIV + ri) * 1024), 16, 0, 0);
+          dma_lds16_gather(lbase + (kNIV + ri) * 1024, src);
         }
       }
     }
@@ -1021,6 +1073,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][TileGeom<FP8, TT>::kTileBytes];
   __shared__ int phys_rows[CONTIG ? 1 : TT];
+  __shared__ int idx_buf[CONTIG ? 1 : kIdxCap];
   constexpr int kRowsWG = 16 * RG * NW;
   const int s = blockIdx.x;
   const int r = blockIdx.y;
@@ -1042,7 +1095,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
   pc.r = r; pc.t0 = t0; pc.qlen = qlen; pc.L = L; pc.row0 = row0;
   pc.seg_start = seg_start; pc.seg_end = min(seg_start + span, L);
   pc.mode = kOutSegment; pc.s = s; pc.prow0 = 0; pc.phase = 0;
-  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, 1, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
+  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, 1, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, idx_buf, pc);
 }
 
 // Work units of request r for a workgroup shape of rows_wg rows and TT-token
@@ -1089,6 +1142,7 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[KS * NBUF][TileGeom<FP8, TT>::kTileBytes];
   __shared__ int phys_rows[CONTIG ? 1 : TT];
+  __shared__ int idx_buf[CONTIG ? 1 : kIdxCap];
   constexpr int kRowsWG = 16 * RG * NW;
   const int lane = threadIdx.x & 63;
   const int R = p.num_reqs;
@@ -1157,7 +1211,7 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
     pc.s = 0;
     pc.prow0 = ((int64_t)gw * 2 + (pos == s_g ? 0 : 1)) * kRowsWG;
     pc.phase = (int)((pos - s_g) % KS);
-    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, KS, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, pc);
+    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, KS, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, idx_buf, pc);
     pos += b - a;
   }
 }
