@@ -553,7 +553,9 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       __syncthreads();  // previous readers of phys_rows are done
       if (threadIdx.x < TT) {
         const int j = tile_start + ((int)threadIdx.x < nvalid ? (int)threadIdx.x : 0);
-        const int blk_i = j / p.block_size;
+        // pages of a power-of-two size (1 for index streams) divide by a shift
+        const int blk_i = (p.block_size & (p.block_size - 1)) == 0 ? j >> __builtin_ctz(p.block_size)
+                                                                     : j / p.block_size;
         const int blk = idx_buf[blk_i - idx_pg0];
         phys_rows[threadIdx.x] =
             (blk < 0 || blk >= p.num_blocks) ? -1 : blk * p.block_size + (j - blk_i * p.block_size);
