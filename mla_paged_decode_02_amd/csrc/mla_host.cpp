@@ -200,16 +200,19 @@ SplitPlan plan_split(const mla_problem* p, int tile) {
   // A batch of equal jobs (every request the same length and query count):
   // k workgroups per (request, row chunk) give every workgroup one piece.  A
   // workgroup that moves to a second piece restarts its stream (the query load
-  // and the first tiles' round trips).  For the stream-bound one-row-group
-  // shape that costs more than leaving up to a quarter of the slots idle
-  // (measured ~6% of the stream kernel at 52 x 16K); shapes with more row
-  // groups lean on the CUs' LDS and matrix units and give up at most 1/8.
+  // and the first tiles' round trips; with gathered tiles also the page
+  // window).  For the stream-bound one-row-group shape, and for gathered
+  // tiles, that costs more than leaving up to a quarter of the slots idle
+  // (measured ~6% of the stream kernel at 52 x 16K, and 22% of the step for
+  // 52 index streams of 2048 keys at 128 heads); contiguous shapes with more
+  // row groups lean on the CUs' LDS and matrix units and give up at most 1/8.
   const int64_t jobs = (int64_t)p->num_reqs * chunks;
   const bool uniform = p->sum_seq_lens > 0 && p->sum_seq_lens == (int64_t)p->num_reqs * p->max_seq_len &&
                        (int64_t)p->num_tokens == (int64_t)p->num_reqs * max_qlen;
   if (uniform && G == slots && jobs <= slots) {
     const int64_t k = slots / jobs;
-    const int64_t num = sp.sh.ks > 1 ? 3 : 7, den = sp.sh.ks > 1 ? 4 : 8;
+    const bool loose = sp.sh.ks > 1 || !sp.sh.contig;
+    const int64_t num = loose ? 3 : 7, den = loose ? 4 : 8;
     if (den * k * jobs >= num * slots) G = k * jobs;
   }
   if (p->max_workgroups > 0 && G > p->max_workgroups) G = p->max_workgroups;

@@ -226,7 +226,8 @@ def test_split_plan_shapes():
 
 def test_split_plan_aligns_uniform_batches():
     # Equal requests: a whole number of workgroups per request (one piece each)
-    # when that keeps >= 3/4 of the slots (one row group) or >= 7/8 (more).
+    # when that keeps >= 3/4 of the slots (one row group, or gathered tiles) or
+    # >= 7/8 (more row groups over contiguous tiles).
     # Without a GPU the planner assumes 256 CUs.
     assert m.split_plan(_split_problem(H=16, R=52, L=200))[0] == 208      # 4 per request
     assert m.split_plan(_split_problem(H=16, R=100, L=200))[0] == 200     # 2 per request
@@ -234,6 +235,8 @@ def test_split_plan_aligns_uniform_batches():
     fp8 = torch.float8_e4m3fn
     assert m.split_plan(_split_problem(H=64, R=52, L=1000, dtype=fp8))[0] == 468  # 9 x 52 of 512
     assert m.split_plan(_split_problem(H=128, R=52, L=200, block=256))[0] == 256  # 208 < 224
+    # gathered tiles (pages smaller than a tile) accept 3/4 at any shape
+    assert m.split_plan(_split_problem(H=128, R=52, L=200, block=1))[0] == 208
     # unequal lengths (the summed lengths say so): every slot
     p = _split_problem(H=16, R=52, L=200)
     p.sum_seq_lens = 52 * 200 - 1
