@@ -1254,9 +1254,13 @@ __device__ __forceinline__ int request_of_token(const int32_t* qo_indptr, int nu
 // workgroups than units some ranges are empty; those wrote nothing and are
 // skipped.  A row whose units all fell in one workgroup was finished there and
 // is skipped here; an empty row gets O = 0 and LSE = -inf (or its sink).
-template <int OUT, bool SPLIT>  // OUT: 0 bf16, 1 fp16, 2 fp32
-__global__ __launch_bounds__(256) void merge_kernel(MergeLaunch p) {
-  constexpr int kBlk = 16;  // pieces in flight per step
+// BLK: pieces in flight per step.  Their registers set the occupancy, so rows
+// that usually have at most 4 pieces take a 4-piece step with six waves per
+// SIMD (rows with more pieces take more steps); the rest take 16 at two.
+template <int OUT, bool SPLIT, int BLK>  // OUT: 0 bf16, 1 fp16, 2 fp32
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BLK <= 4 ? 6 : 2, 8)))
+void merge_kernel(MergeLaunch p) {
+  constexpr int kBlk = BLK;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (int64_t)p.num_tokens * p.num_heads) return;
@@ -1600,13 +1604,27 @@ hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, int s
                    : launch_seg_shape<false, false>(a, sh, split_wgs, stream);
 }
 
-template <bool SPLIT>
+template <bool SPLIT, int BLK>
 void launch_merge_t(const MergeLaunch& a, dim3 grid, hipStream_t stream) {
   switch (a.out_dtype) {
-    case 0: hipLaunchKernelGGL((merge_kernel<0, SPLIT>), grid, dim3(256), 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((merge_kernel<1, SPLIT>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((merge_kernel<2, SPLIT>), grid, dim3(256), 0, stream, a); break;
+    case 0: hipLaunchKernelGGL((merge_kernel<0, SPLIT, BLK>), grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((merge_kernel<1, SPLIT, BLK>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((merge_kernel<2, SPLIT, BLK>), grid, dim3(256), 0, stream, a); break;
   }
+}
+
+// Pieces a row usually has: the segment count, or for split pieces the
+// workgroups per request (+2 when a request's range does not start and end on
+// workgroup boundaries).
+template <bool SPLIT>
+void launch_merge_b(const MergeLaunch& a, dim3 grid, hipStream_t stream) {
+  int est = a.num_segments;
+  if (SPLIT) {
+    const int r = a.num_reqs > 0 ? a.num_reqs : 1;
+    est = a.grid_wgs / r + (a.grid_wgs % r ? 2 : 0);
+  }
+  if (est <= 4) launch_merge_t<SPLIT, 4>(a, grid, stream);
+  else launch_merge_t<SPLIT, 16>(a, grid, stream);
 }
 
 template <int IN>
@@ -1632,8 +1650,8 @@ hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream) {
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_tokens * a.num_heads;
   dim3 grid((unsigned)((rows + 3) / 4));
-  if (a.unit_offsets) launch_merge_t<true>(a, grid, stream);
-  else launch_merge_t<false>(a, grid, stream);
+  if (a.unit_offsets) launch_merge_b<true>(a, grid, stream);
+  else launch_merge_b<false>(a, grid, stream);
   return hipGetLastError();
 }
 
