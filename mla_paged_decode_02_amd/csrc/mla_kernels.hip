@@ -1255,8 +1255,9 @@ __device__ __forceinline__ int request_of_token(const int32_t* qo_indptr, int nu
 // skipped.  A row whose units all fell in one workgroup was finished there and
 // is skipped here; an empty row gets O = 0 and LSE = -inf (or its sink).
 // BLK: pieces in flight per step.  Their registers set the occupancy, so rows
-// that usually have at most 4 pieces take a 4-piece step with six waves per
-// SIMD (rows with more pieces take more steps); the rest take 16 at two.
+// that usually have at most 12 pieces take 4-piece steps with six waves per
+// SIMD (measured faster than one 16-piece step at two waves up to 9 pieces);
+// the rest take 16-piece steps.
 template <int OUT, bool SPLIT, int BLK>  // OUT: 0 bf16, 1 fp16, 2 fp32
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BLK <= 4 ? 6 : 2, 8)))
 void merge_kernel(MergeLaunch p) {
@@ -1623,7 +1624,7 @@ void launch_merge_b(const MergeLaunch& a, dim3 grid, hipStream_t stream) {
     const int r = a.num_reqs > 0 ? a.num_reqs : 1;
     est = a.grid_wgs / r + (a.grid_wgs % r ? 2 : 0);
   }
-  if (est <= 4) launch_merge_t<SPLIT, 4>(a, grid, stream);
+  if (est <= 12) launch_merge_t<SPLIT, 4>(a, grid, stream);
   else launch_merge_t<SPLIT, 16>(a, grid, stream);
 }
 
