@@ -268,6 +268,31 @@ def test_split_parity_sweep(case, wgs):
                  ref_o, ref_l)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_split_long_row_among_short_ones(dtype):
+    """One long request among many short ones: the merge's step size follows
+    the usual piece count per row (small here), while the long request's rows
+    gather far more than 64 pieces (the merge's long-row path)."""
+    import mla_paged_decode_02_amd as m
+    lens = [16] * 60 + [40000]
+    _print_case(f"long row among short ones {dtype} lens=60x16+40000")
+    w = mi.make_workload(name="longrow", seq_lens=lens, num_heads=16, block_size=64, dtype=dtype,
+                         sinks=True, seed=77 if dtype == "bf16" else 78)
+    d = mi.to_torch(w, "cuda")
+    args = mi.call_args(w, d)
+    out, lse = m.decode(**args, sinks=d["sinks"], num_segments=0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    g, rows_wg, tt = m.split_plan(m.make_problem(**args, num_segments=0))
+    assert (40000 // tt) * g // (sum(-(-n // tt) for n in lens)) > 64  # the long row's pieces
+    ref_o, ref_l = orc.mla_decode(w, reqs=[0, 59, 60])
+    sel = [0, 59, 60]
+    o = out.cpu().numpy().astype(np.float64)[sel]
+    l = lse.cpu().numpy().astype(np.float64)[sel]
+    vm = vmax(w, sel)
+    assert np.abs(o - ref_o[sel]).max() <= out_tol(w) * vm
+    assert np.abs(l - ref_l[sel]).max() <= LSE_TOL
+
+
 @pytest.mark.parametrize("wgs", [0, 2, 5, 13])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
 def test_split_counts_every_key_once(dtype, wgs):
