@@ -633,11 +633,12 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   // LDS operands are prefetched several MFMA steps ahead: one MFMA issues every
   // 16-32 cycles, while an LDS read takes ~100-200 cycles to return.  (Kernels
   // sized for two waves per SIMD have half the registers: shallower there.)
-  // (bf16 with two waves per SIMD: two steps ahead, which keeps the Q, S and
-  // accumulator registers clear of spills.)
+  // (bf16 with two waves per SIMD: K operands two steps ahead and Vt operands
+  // four, which keeps the Q, S and accumulator registers clear of spills in
+  // the tile loop.)
   constexpr int kPF = OCC == 2 ? (FP8 ? 4 : 2) : 8;
   constexpr int kPFL = OCC == 2 ? 2 : 4;
-  constexpr int kPFV = OCC == 2 ? (FP8 ? 4 : 2) : 8;
+  constexpr int kPFV = OCC == 2 ? 4 : 8;
   typedef typename std::conditional<kNB == 2, bf16x8, i16x4>::type POp;
   typedef typename std::conditional<FP8, i32x2, POp>::type VRaw;
   typedef f32x4 Acc[RG][32];
