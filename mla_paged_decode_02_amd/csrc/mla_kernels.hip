@@ -1256,11 +1256,11 @@ __device__ __forceinline__ int request_of_token(const int32_t* qo_indptr, int nu
 // skipped.  A row whose units all fell in one workgroup was finished there and
 // is skipped here; an empty row gets O = 0 and LSE = -inf (or its sink).
 // BLK: pieces in flight per step.  Their registers set the occupancy, so rows
-// that usually have at most 12 pieces take 4-piece steps with six waves per
-// SIMD (measured faster than one 16-piece step at two waves up to 9 pieces);
-// the rest take 16-piece steps.
+// that usually have at most 12 pieces take 4-piece steps with five waves per
+// SIMD (measured faster than one 16-piece step at two waves up to 9 pieces;
+// six waves spill); the rest take 16-piece steps.
 template <int OUT, bool SPLIT, int BLK>  // OUT: 0 bf16, 1 fp16, 2 fp32
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BLK <= 4 ? 6 : 2, 8)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BLK <= 4 ? 5 : 2, 8)))
 void merge_kernel(MergeLaunch p) {
   constexpr int kBlk = BLK;
   const int lane = threadIdx.x & 63;
