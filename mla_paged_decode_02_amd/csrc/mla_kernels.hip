@@ -462,16 +462,19 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   // it waits for all of the wave's loads (the window is refilled at most once
   // per kIdxCap pages).  Entries past the table repeat its last one.
   int idx_pg0 = 0x7fffffff / 2;
-  auto load_idx = [&](int pg) {
+  auto issue_idx = [&](int pg) {
     const int npages = max(cap / p.block_size, 1);
     const int64_t stride = p.bt_stride_col;
     const i32x4 trs = make_rsrc(p.block_table + bt_base,
                                 (int)min((int64_t)0x7fffffff, ((int64_t)(npages - 1) * stride + 1) * 4));
-    __syncthreads();  // every wave is done with the previous window
     for (int i = wave; i < kIdxCap / 64; i += NW) {
       const int e = min(pg + i * 64 + lane, npages - 1);
       dma_lds4(trs, lds_address(idx_buf) + (unsigned)(i * 256), (int)((int64_t)e * stride * 4));
     }
+  };
+  auto load_idx = [&](int pg) {
+    __syncthreads();  // every wave is done with the previous window
+    issue_idx(pg);
     wait_vmcnt<0>();
     __syncthreads();
     idx_pg0 = pg;
@@ -964,7 +967,15 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     QLat qlat;
     QRope qrope;
     load_q(qop, qlat, qrope);
+    // Gathered tiles: the first page window loads in the same round trip as q
+    // (the previous piece ended with a barrier, so nobody reads the window).
+    const bool early_idx = !CONTIG && ntiles > 0;
+    if (early_idx) issue_idx(seg_start / p.block_size);
     wait_vmcnt<0>();  // q is in registers before the DMA stream starts
+    if (early_idx) {
+      __syncthreads();
+      idx_pg0 = seg_start / p.block_size;
+    }
     Acc acc;
 #pragma unroll
     for (int q = 0; q < RG; ++q)
