@@ -351,6 +351,15 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     end_min[q] = min(__builtin_amdgcn_readfirstlane(v), eff_end);
   }
 
+  // fp8 four-wave workgroups whose chunk leaves a wave without rows (48
+  // heads): that wave issues every DMA instruction of a tile, so the waves
+  // that compute issue none.  (Eight waves would need more than vmcnt's 63
+  // outstanding loads in one wave; the bf16 variant spills.)
+  constexpr bool kProd = FP8 && CONTIG && KS == 1 && NW == 4;
+  const int active_waves = cdiv(min(M - row0, kRowsWG), 16 * RG);
+  const bool prod_mode = kProd && active_waves < NW;
+  const bool is_producer = prod_mode && wave == NW - 1;
+
   const float qs = p.q_scale ? *p.q_scale : 1.0f;
   const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
   const float sl2 = p.softmax_scale * kLog2e * qs * ks;
@@ -514,29 +523,39 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       auto dma_all = [&](auto full_tag) {
         constexpr bool kFull = decltype(full_tag)::value;
         auto clamp = [&](int row) { return kFull ? row : (row < nvalid ? row : 0); };
-#pragma unroll
-        for (int i = 0; i < kVPerWave; ++i) {
-          const int vi = wave + NW * i;
+        auto dma_v = [&](int vi) {
           int voff, soff;
           if constexpr (!FP8) {
             soff = clamp(vi) * kRowBytes;
-            voff = key16 ^ (16 * F::swz_v(vi));
+            voff = opaque(key16) ^ (16 * F::swz_v(vi));
           } else {
             // rows 2vi (lanes 0-31) and 2vi+1 (lanes 32-63); F::swz_v(2vi+1) = F::swz_v(2vi) ^ 2
-            const int row = 2 * vi + v_half;
+            const int half = opaque(v_half);
+            const int row = 2 * vi + half;
             soff = 0;
-            voff = clamp(row) * kRowBytes + ((16 * v_cpos) ^ (32 * v_half) ^ (16 * F::swz_v(2 * vi)));
+            voff = clamp(row) * kRowBytes + (opaque((16 * v_cpos) ^ (32 * v_half)) ^ (16 * F::swz_v(2 * vi)));
           }
           dma_lds16(rsrc, lbase + vi * 1024, voff, soff);
-        }
+        };
+        auto dma_r = [&](int ri) {
+          const int row = ri * kRowsPerRope + rope_row_in;
+          const int voff = clamp(row) * kRowBytes + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
+          dma_lds16(rsrc, lbase + (kNIV + ri) * 1024, voff, 0);
+        };
+        if (prod_mode) {
+          // A wave without rows issues the whole tile; the others none.
+          if (is_producer) {
 #pragma unroll
-        for (int i = 0; i < kRopePerWaveMax; ++i) {
-          const int ri = wave + NW * i;
-          if (ri < kNIR) {
-            const int row = ri * kRowsPerRope + rope_row_in;
-            const int voff = clamp(row) * kRowBytes + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
-            dma_lds16(rsrc, lbase + (kNIV + ri) * 1024, voff, 0);
+            for (int vi = 0; vi < kNIV; ++vi) dma_v(vi);
+#pragma unroll
+            for (int ri = 0; ri < kNIR; ++ri) dma_r(ri);
           }
+        } else {
+#pragma unroll
+          for (int i = 0; i < kVPerWave; ++i) dma_v(wave + NW * i);
+#pragma unroll
+          for (int i = 0; i < kRopePerWaveMax; ++i)
+            if (wave + NW * i < kNIR) dma_r(wave + NW * i);
         }
       };
       dma_all(std::false_type{});
@@ -1003,7 +1022,8 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         if (k + NBUF - 1 < nloc) issue_tile(tile_of(k + NBUF - 1), slot0 + (k + NBUF - 1) % NBUF);
         wait_tiles<kNIw, NBUF - 1>(min(NBUF - 1, nloc - 1 - k));
       } else {
-        wait_tiles<kNIw, (NBUF >= 2 ? NBUF - 2 : 0)>(min(NBUF - 2, ntiles - 1 - k));
+        if (is_producer) wait_tiles<kNI, (NBUF >= 2 ? NBUF - 2 : 0)>(min(NBUF - 2, ntiles - 1 - k));
+        else wait_tiles<kNIw, (NBUF >= 2 ? NBUF - 2 : 0)>(min(NBUF - 2, ntiles - 1 - k));
         __syncthreads();
         if (k + NBUF - 1 < ntiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
       }
