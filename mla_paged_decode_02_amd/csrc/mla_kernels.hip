@@ -525,15 +525,17 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         auto clamp = [&](int row) { return kFull ? row : (row < nvalid ? row : 0); };
         auto dma_v = [&](int vi) {
           int voff, soff;
+          // (the producer's lane offsets are formed per instruction, not held
+          // for all of a tile's rows)
+          auto keep = [&](int v) { return kProd ? opaque(v) : v; };
           if constexpr (!FP8) {
             soff = clamp(vi) * kRowBytes;
-            voff = opaque(key16) ^ (16 * F::swz_v(vi));
+            voff = key16 ^ (16 * F::swz_v(vi));
           } else {
             // rows 2vi (lanes 0-31) and 2vi+1 (lanes 32-63); F::swz_v(2vi+1) = F::swz_v(2vi) ^ 2
-            const int half = opaque(v_half);
-            const int row = 2 * vi + half;
+            const int row = 2 * vi + keep(v_half);
             soff = 0;
-            voff = clamp(row) * kRowBytes + (opaque((16 * v_cpos) ^ (32 * v_half)) ^ (16 * F::swz_v(2 * vi)));
+            voff = clamp(row) * kRowBytes + (keep((16 * v_cpos) ^ (32 * v_half)) ^ (16 * F::swz_v(2 * vi)));
           }
           dma_lds16(rsrc, lbase + vi * 1024, voff, soff);
         };
