@@ -154,6 +154,9 @@ SWEEP = [
     # more pages on (48 < 4 waves x 16 keys, 96 < 4 waves x 32 keys)
     ("bf16", 16, 48, [777, 100, 48], None, False, False, 3),
     ("fp8_e4m3", 16, 96, [1000, 300, 97], None, False, True, 3),
+    # four-wave chunks with waves that hold no rows (40 heads; qlen 2 leaves a
+    # 16-row chunk): a row-less wave issues the whole tile's loads
+    ("fp8_e4m3", 40, 64, [900, 130], [2, 1], True, True, 3),
 ]
 
 
