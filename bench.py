@@ -1,19 +1,22 @@
 #!/usr/bin/env python3
 """MLA paged decode benchmark on one MI355X.
 
-One step = one full decode of the batch: the segment kernel (paged KV stream,
-QK^T, base-2 online softmax, P.V, per-segment partials) and the merge kernel
-(output + natural-log LSE), i.e. mla_decode through the C ABI.
+One step = one full decode of the batch through the C ABI (mla_decode): the
+stream kernel (paged KV stream, Q.K^T, base-2 online softmax, P.V, partials
+or finished rows) and the merge kernel (output + natural-log LSE, sinks).
 
-Default workload: bs=52 requests, qlen=1, 16 heads, 16384 KV tokens per
+Headline workload: bs=52 requests, qlen=1, 16 heads, 16384 KV tokens per
 request, bf16 q and latent cache ~N(0,1), block 64 = TILE 64, random block
-table permutation, segment count from the planner, scale 1/sqrt(192).
+table permutation, scale 1/sqrt(192), balanced split.  The default run also
+times every other benchmark configuration (16-head fp8, 48- and 64-head fp8,
+128-head bf16 with 256-token blocks, the ragged 128-request causal batch)
+under both schedules (the balanced split and the segment partition at the
+planner's S) and appends them under "extra", each with its own roofline.
+--extra adds the fused q prologue, the index streams and the DCP emulation.
+
 Inputs are synthetic (seeded) and resident in HBM before timing starts; two
 cache copies alternate between steps so no step reuses the previous step's
-cache lines from the 256 MB last-level cache.
-
-Prints ONE JSON line.  Extra configurations (--extra) are appended under
-"extra" in the same line.
+cache lines from the 256 MB last-level cache.  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -53,10 +56,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--extra", action="store_true", help="also time the other bs=52 workloads")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the q prologue, index-stream and DCP workloads")
+    ap.add_argument("--only", action="store_true", help="time the --workload alone (no other configurations)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-reqs", type=int, default=0, help="requests the oracle times (0 = all)")
-    ap.add_argument("--num-segments", type=int, default=0)
+    ap.add_argument("--schedule", default="balanced", choices=["balanced", "segments"],
+                    help="schedule of the headline line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -121,7 +127,7 @@ def time_dcp(name, args, torch, m, mi):
     so = torch.empty((W, T, H, 512), dtype=torch.bfloat16, device="cuda")
     sl = torch.empty((W, T, H), dtype=torch.float32, device="cuda")
     # each shard decodes straight into its slice of the stacked buffers
-    decs = [m.Decoder(**mi.call_args(sw, d), sinks=None, num_segments=0, out=so[k], lse=sl[k])
+    decs = [m.Decoder(**mi.call_args(sw, d), sinks=None, schedule="balanced", out=so[k], lse=sl[k])
             for k, (sw, d) in enumerate(zip(shards, ds))]
     sinks = torch.randn(H, generator=torch.Generator().manual_seed(11)).cuda()
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
@@ -156,100 +162,100 @@ def time_dcp(name, args, torch, m, mi):
             "split_workgroups": decs[0].split_workgroups}
 
 
-def time_workload(name, args, torch, m, mi, want_roofline):
-    w, ds = build_inputs(name, torch, mi)
-    esz = 2 if w.kv_dtype == "bf16" else 1
-    kv_bytes = w.kv_bytes_touched()
-    calls = [mi.call_args(w, d) for d in ds]
-    # One prepared call per cache copy: each step is a single C call.
-    decs = [m.Decoder(**c, sinks=d["sinks"], num_segments=args.num_segments, out_dtype=torch.bfloat16)
-            for c, d in zip(calls, ds)]
-    S = decs[0].num_segments
-    stream = torch.cuda.current_stream()
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # dense fp8 MFMA peak of MI355X
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
 
-    def step(i):
-        decs[i & 1].run(stream)
 
-    warm_s = warmup(step, args.warmup, torch)
+def attention_flops(w):
+    """MFMA work of one decode step: per (query row, visible key) 576 MACs of
+    Q.K^T and 512 of P.V, 2 flops each."""
+    qo = [int(x) for x in w.qo_indptr]
+    rows_keys = 0
+    for r, L in enumerate(int(x) for x in w.seq_lens):
+        ql = qo[r + 1] - qo[r]
+        for i in range(ql):
+            rows_keys += max(0, L - ql + i + 1) if w.causal else L
+    return 2.0 * w.num_heads * rows_keys * (576 + 512)
+
+
+def timed_loop(fn, args, torch, stream):
+    """Warm-up, then args.steps calls bracketed by events on `stream`: mean us."""
+    warmup(fn, args.warmup, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     e0.record(stream)
     for i in range(args.steps):
-        step(i)
+        fn(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    return e0.elapsed_time(e1) / args.steps * 1e3
 
-    res = {"workload": name, "num_heads": w.num_heads, "dtype": w.kv_dtype, "num_segments": S,
-           "split_workgroups": decs[0].split_workgroups,
-           "num_reqs": w.num_reqs, "num_tokens": w.num_tokens, "max_qlen": w.max_qlen,
-           "max_seq_len": w.max_seq_len, "block_size": w.block_size, "causal": bool(w.causal),
-           "sinks": w.sinks is not None,
-           "us_per_step": ms * 1e3, "kv_bytes": kv_bytes, "warmup_s": round(warm_s, 3),
-           "eff_kv_GBps": kv_bytes / (ms * 1e-3) / 1e9,
-           "frac_of_hbm_peak": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    if not want_roofline:
-        return w, res, None
 
+def time_schedule(w, ds, calls, schedule, args, torch, m, stream):
+    """One schedule of one workload: the fused step, then each launch alone,
+    with the dominant (stream) kernel's roofline."""
+    kv_bytes = w.kv_bytes_touched()
+    decs = [m.Decoder(**c, sinks=d["sinks"], schedule=schedule, out_dtype=torch.bfloat16)
+            for c, d in zip(calls, ds)]
+    us = timed_loop(lambda i: decs[i & 1].run(stream), args, torch, stream)
+    stage_us = {st: timed_loop(lambda i, st=st: decs[i & 1].run_stage(st, stream), args, torch, stream)
+                for st in (1, 2)}
+    esz = 2 if w.kv_dtype == "bf16" else 1
     T, H = w.num_tokens, w.num_heads
-    out_esz = 2  # bf16 output
     q_bytes = T * H * 576 * esz
+    res = {"schedule": schedule, "us_per_step": round(us, 2),
+           "eff_kv_GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+           "kv_frac_of_hbm_peak": round(kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "stream_kernel_us": round(stage_us[1], 2), "merge_kernel_us": round(stage_us[2], 2)}
     if decs[0].split is not None:
-        # Balanced split: stage 1 (the cache stream, the dominant kernel) and
-        # stage 2 (the merge of requests cut by a range boundary), each timed
-        # alone with events on the stream it is launched on.
-        stage_us = {}
-        for stage in (1, 2):
-            warmup(lambda i: decs[i & 1].run_stage(stage, stream), args.warmup, torch)
-            e0.record(stream)
-            for i in range(args.steps):
-                decs[i & 1].run_stage(stage, stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            stage_us[stage] = e0.elapsed_time(e1) / args.steps * 1e3
         sched = split_schedule(w, *decs[0].split)
-        alg = kv_bytes + q_bytes + sched["final_rows"] * (512 * out_esz + 4) + sched["partial_rows"] * (512 + 2) * 4
-        kernel, kernel_us = "split_kernel", stage_us[1]
+        alg = kv_bytes + q_bytes + sched["final_rows"] * (512 * 2 + 4) + sched["partial_rows"] * (512 + 2) * 4
+        kernel = "split_kernel"
         res["split"] = {"workgroups": decs[0].split[0], "rows_per_workgroup": decs[0].split[1],
                         "unit_keys": decs[0].split[2], **sched}
-        res["merge_kernel_us"] = stage_us[2]
     else:
-        # Segment partition: segment kernel and merge kernel each timed alone.
         S = decs[0].num_segments
-        so = torch.empty((T, H, S, 512), dtype=torch.float32, device="cuda")
-        sm = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
-        se = torch.empty((T, H, S), dtype=torch.float32, device="cuda")
-        warmup(lambda i: m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
-                                           segm_expsum=se, stream=stream), args.warmup, torch)
-        e0.record(stream)
-        for i in range(args.steps):
-            m.decode_segments(**calls[i & 1], num_segments=S, segm_output=so, segm_max=sm,
-                              segm_expsum=se, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        seg_ms = e0.elapsed_time(e1) / args.steps
-        qlens = torch.diff(ds[0]["qo_indptr"])
-        part_lens = torch.repeat_interleave(ds[0]["seq_lens"], qlens).to(torch.int32)
-        mo = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
-        ml = torch.empty((T, H), dtype=torch.float32, device="cuda")
         tile = w.tile_size or m.tile_size_for_block(w.block_size)
-        warmup(lambda i: m.merge_segments(so, sm, se, part_lens, tile, sinks=ds[0]["sinks"], out=mo, lse=ml,
-                                          stream=stream), args.warmup, torch)
-        e0.record(stream)
-        for i in range(args.steps):
-            m.merge_segments(so, sm, se, part_lens, tile, sinks=ds[0]["sinks"], out=mo, lse=ml, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        res["merge_kernel_us"] = e0.elapsed_time(e1) / args.steps * 1e3
         qlen_r = [int(x) for x in (w.qo_indptr[1:] - w.qo_indptr[:-1])]
         valid = sum(ql * len(m.segment_bounds(int(L), S, tile)) for L, ql in zip(w.seq_lens, qlen_r))
         alg = kv_bytes + q_bytes + valid * H * (512 + 2) * 4
-        kernel, kernel_us = "segment_kernel", seg_ms * 1e3
-    achieved = alg / (kernel_us * 1e-6) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(name),
-            "kernel": kernel, "kernel_us": round(kernel_us, 2), "algorithmic_bytes": int(alg)}
-    res["segment_kernel_us"] = kernel_us
-    return w, res, roof
+        kernel = "segment_kernel"
+        res["num_segments"] = S
+        res["segments_valid_rows"] = valid * H
+    ach = alg / (stage_us[1] * 1e-6) / 1e9
+    flops = attention_flops(w)
+    peak_mfma = FP8_MFMA_PEAK_TFLOPS if w.kv_dtype != "bf16" else BF16_MFMA_PEAK_TFLOPS
+    t_hbm = alg / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (peak_mfma * 1e12)
+    if t_mfma > t_hbm:
+        # more MFMA work than HBM traffic at the two peaks: the matrix cores bound it
+        roof = {"bound": "mfma", "achieved": round(flops / (stage_us[1] * 1e-6) / 1e12, 1),
+                "peak": peak_mfma, "unit": "TFLOP/s", "frac": round(t_mfma / (stage_us[1] * 1e-6), 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": profiled_traffic(w.name, schedule), "kernel": kernel,
+                 "kernel_us": round(stage_us[1], 2), "algorithmic_bytes": int(alg),
+                 "hbm_bytes_per_s": round(ach, 1), "flops": round(flops), "mfma_tflops": round(
+                     flops / (stage_us[1] * 1e-6) / 1e12, 1)})
+    res["roofline"] = roof
+    del decs
+    return res
+
+
+def time_workload(name, args, torch, m, mi, schedules):
+    """Every requested schedule of one workload on the same resident inputs."""
+    w, ds = build_inputs(name, torch, mi)
+    calls = [mi.call_args(w, d) for d in ds]
+    stream = torch.cuda.current_stream()
+    base = {"workload": name, "num_heads": w.num_heads, "dtype": w.kv_dtype,
+            "num_reqs": w.num_reqs, "num_tokens": w.num_tokens, "max_qlen": w.max_qlen,
+            "max_seq_len": w.max_seq_len, "block_size": w.block_size, "causal": bool(w.causal),
+            "sinks": w.sinks is not None, "kv_bytes": w.kv_bytes_touched()}
+    out = [dict(base, **time_schedule(w, ds, calls, sch, args, torch, m, stream)) for sch in schedules]
+    del ds, calls
+    torch.cuda.empty_cache()
+    return w, out
 
 
 def split_schedule(w, G, rows_wg, tt):
@@ -286,10 +292,11 @@ def split_schedule(w, G, rows_wg, tt):
 KERNEL_SOURCES = ("mla_paged_decode_02_amd/csrc/mla_kernels.hip", "mla_paged_decode_02_amd/csrc/mla_internal.h")
 
 
-def profiled_traffic(workload):
-    """HBM bytes per segment-kernel launch from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary of this workload (copy-calibrated), or
-    None when there is none or the kernel sources changed since it was taken."""
+def profiled_traffic(workload, schedule="balanced"):
+    """HBM bytes per stream-kernel launch from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary of this workload and schedule
+    (copy-calibrated), or None when there is none or the kernel sources
+    changed since it was taken."""
     import glob
     import hashlib
 
@@ -305,8 +312,8 @@ def profiled_traffic(workload):
                 if ":" in line and not line.startswith(("|", "#", " ")):
                     k, _, v = line.partition(":")
                     kv[k.strip()] = v.strip()
-        if (kv.get("workload") == workload and kv.get("kernel_source_sha256_16") == digest
-                and "stream_kernel_traffic_bytes" in kv):
+        if (kv.get("workload") == workload and kv.get("schedule", "balanced") == schedule
+                and kv.get("kernel_source_sha256_16") == digest and "stream_kernel_traffic_bytes" in kv):
             return int(kv["stream_kernel_traffic_bytes"])
     return None
 
@@ -339,6 +346,15 @@ def cpu_baseline(w, nreq, min_runs=3, min_total_s=10.0, max_runs=15):
                       f"({sum(times):.1f} s in all)"}
 
 
+# The benchmark configurations of the decode measurements (bs=52 x 16K at
+# 16..128 heads, and the ragged causal batch): each is timed under both
+# schedules in the default run.
+CORE = ["bs52_ctx16k_h16_bf16_blk64", "bs52_ctx16k_h16_fp8_blk64", "bs52_ctx16k_h48_fp8_blk64",
+        "bs52_ctx16k_h64_fp8_blk64", "bs52_ctx16k_h128_bf16_blk256", "ragged128_max32k_h96_fp8_causal_sinks"]
+OPTIONAL = ["bs52_ctx16k_h48_fp8_blk64_bf16q", "sparse_bs52_top2048_ctx16k_h16_bf16",
+            "sparse_bs52_top2048_ctx16k_h128_fp8"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -355,45 +371,53 @@ def main():
         return
     m.lib()
     t0 = time.time()
-    w, res, roof = time_workload(args.workload, args, torch, m, mi, want_roofline=True)
-    extra = []
-    if args.extra:
-        for name in WORKLOADS:
-            if name == args.workload:
-                continue
-            torch.cuda.empty_cache()
-            _, r2, _ = time_workload(name, args, torch, m, mi, want_roofline=False)
-            extra.append(r2)
-        for name in DCP_WORKLOADS:
-            torch.cuda.empty_cache()
-            extra.append(time_dcp(name, args, torch, m, mi))
+    other = "segments" if args.schedule == "balanced" else "balanced"
+    w, lines = time_workload(args.workload, args, torch, m, mi,
+                             [args.schedule] if args.only else [args.schedule, other])
+    head = lines[0]
+    print(f"[bench] {args.workload} {args.schedule}: {head['us_per_step']} us/step", file=sys.stderr, flush=True)
+    extra = lines[1:]
+    if not args.only:
+        names = [n for n in CORE if n != args.workload]
+        if args.extra:
+            names += [n for n in OPTIONAL if n != args.workload]
+        for name in names:
+            scheds = ["balanced", "segments"] if name in CORE else ["balanced"]
+            _, ls = time_workload(name, args, torch, m, mi, scheds)
+            for ln in ls:
+                print(f"[bench] {name} {ln['schedule']}: {ln['us_per_step']} us/step", file=sys.stderr,
+                      flush=True)
+            extra += ls
+        if args.extra:
+            for name in DCP_WORKLOADS:
+                torch.cuda.empty_cache()
+                extra.append(time_dcp(name, args, torch, m, mi))
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_reqs)
+    roof = dict(head["roofline"])
     line = {
         "metric": METRIC,
-        "value": round(res["eff_kv_GBps"], 1),
+        "value": head["eff_kv_GBps"],
         "unit": "GB/s (effective KV bytes / step time)",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_s": res["warmup_s"],
-        "ms_per_step": round(res["us_per_step"] / 1e3, 5),
-        "us_per_step": round(res["us_per_step"], 2),
+        "ms_per_step": round(head["us_per_step"] / 1e3, 5),
+        "us_per_step": head["us_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8_e4m3",
         "data": "synthetic (seeded N(0,1) q and latent cache, random page permutation)",
-        "config": {"workload": res["workload"], "batch": res["num_reqs"], "tokens": res["num_tokens"],
-                   "max_qlen": res["max_qlen"], "max_kv_tokens_per_request": res["max_seq_len"],
-                   "num_heads": res["num_heads"], "block_size": res["block_size"],
-                   "causal": res["causal"], "sinks": res["sinks"],
-                   "num_segments": res["num_segments"], "split_workgroups": res["split_workgroups"],
+        "config": {"workload": head["workload"], "schedule": head["schedule"], "batch": head["num_reqs"],
+                   "tokens": head["num_tokens"], "max_qlen": head["max_qlen"],
+                   "max_kv_tokens_per_request": head["max_seq_len"], "num_heads": head["num_heads"],
+                   "block_size": head["block_size"], "causal": head["causal"], "sinks": head["sinks"],
                    "parallelism": "single GPU"},
-        "frac_of_hbm_peak": round(res["frac_of_hbm_peak"], 4),
+        "kv_frac_of_hbm_peak": head["kv_frac_of_hbm_peak"],
         "roofline": roof,
-        "stream_kernel_us": round(res.get("segment_kernel_us", 0.0), 2),
-        "merge_kernel_us": round(res.get("merge_kernel_us", 0.0), 2),
-        "split": res.get("split"),
+        "stream_kernel_us": head["stream_kernel_us"],
+        "merge_kernel_us": head["merge_kernel_us"],
+        "split": head.get("split"),
         "cpu_baseline": cpu,
         "extra": extra,
         "wall_s": round(time.time() - t0, 1),

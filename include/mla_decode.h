@@ -64,6 +64,11 @@ extern "C" {
 #define MLA_MAX_SEGMENTS 256
 #define MLA_MAX_TILE 128
 
+/* How mla_decode splits the key axis (mla_problem.schedule). */
+#define MLA_SCHEDULE_SEGMENTS 0 /* the segment partition of the merge page's module
+                                   description, S = num_segments (0 = the planner's S) */
+#define MLA_SCHEDULE_BALANCED 1 /* equal key ranges per workgroup (num_segments must be 0) */
+
 /*
  * One decode batch.  Set struct_size = sizeof(mla_problem); zero-fill unused
  * fields.  Rows of a request: its qlen new query tokens x num_heads.
@@ -117,7 +122,9 @@ typedef struct mla_problem {
   float softmax_scale; /* scores = softmax_scale * (q . row) over all 576 dims */
   int32_t tile_size;   /* 0 = min(128, largest power-of-two divisor of block_size);
                           else a power of two <= 128 dividing block_size */
-  int32_t num_segments; /* S >= 1 (mla_decode also accepts 0 = balanced split) */
+  int32_t num_segments; /* S >= 1; mla_decode also accepts 0: the planner picks S
+                           (mla_resolve_num_segments), or the balanced split
+                           when schedule == MLA_SCHEDULE_BALANCED */
   int32_t max_workgroups; /* balanced split: at most this many workgroups
                              (0 = as many as the device holds at once), e.g.
                              to leave compute units to concurrent work */
@@ -147,6 +154,11 @@ typedef struct mla_problem {
   const void* q_pe;
   int64_t q_pe_stride_token;
   int64_t q_pe_stride_head;
+
+  /* mla_decode only: MLA_SCHEDULE_SEGMENTS (0, the segment partition) or
+   * MLA_SCHEDULE_BALANCED (1, see mla_decode).  The segment entry points
+   * require 0. */
+  int32_t schedule;
 } mla_problem;
 
 /*
@@ -217,9 +229,12 @@ int mla_combine_lse(const void* shard_out, int32_t in_dtype, const float* shard_
  * (>= mla_decode_workspace_bytes(p) bytes, 256-byte aligned; its contents on
  * entry do not matter).  sinks / out / out_dtype / lse as for
  * mla_merge_segments.
- *  - num_segments >= 1: the segment partition above with that S, then the
- *    merge (the same results as mla_decode_segments + mla_merge_segments).
- *  - num_segments == 0: a balanced split of the key axis.  The batch's work is
+ *  - schedule MLA_SCHEDULE_SEGMENTS: the segment partition above with
+ *    S = num_segments, or with the planner's S (mla_resolve_num_segments) when
+ *    num_segments == 0, then the merge (the same results as
+ *    mla_decode_segments + mla_merge_segments with that S).
+ *  - schedule MLA_SCHEDULE_BALANCED (num_segments must be 0): a balanced
+ *    split of the key axis.  The batch's work is
  *    one sequence of units (request, row chunk, tile of TT keys) that is cut
  *    into equal ranges, one per workgroup, so every compute unit streams the
  *    same number of cache rows whatever the lengths.  A (request, row chunk)
@@ -244,16 +259,16 @@ int mla_decode_stage(const mla_problem* p, const float* sinks, void* out, int32_
 /* Workspace mla_decode needs for p.  Returns 0 and sets *bytes, or an error. */
 int mla_decode_workspace_bytes(const mla_problem* p, size_t* bytes);
 
-/* The balanced split mla_decode uses for p (num_segments == 0): workgroups,
+/* The balanced split mla_decode uses for p (schedule MLA_SCHEDULE_BALANCED): workgroups,
  * query rows per workgroup and keys per unit (TT).  Returns 1 and fills the
  * outputs (each may be NULL); 0 when p uses the segment partition instead;
  * or an error. */
 int mla_split_plan(const mla_problem* p, int32_t* workgroups, int32_t* rows_per_workgroup,
                    int32_t* unit_keys);
 
-/* The S the planner gives p when num_segments == 0 (for the segment entry
- * points; host only after the first call on a device: reads the CU count
- * once), else p->num_segments.  Returns S >= 1 or an error. */
+/* The S mla_decode uses for p under MLA_SCHEDULE_SEGMENTS: the planner's S
+ * when num_segments == 0 (host only after the first call on a device: reads
+ * the CU count once), else p->num_segments.  Returns S >= 1 or an error. */
 int mla_resolve_num_segments(const mla_problem* p);
 
 /* Planner (pure host): S so that request x segment work items fill num_cus

@@ -36,6 +36,10 @@ MLA_DTYPE_FP8_E4M3 = 2
 MLA_DTYPE_FP16 = 3
 MLA_DTYPE_FP32 = 4
 
+MLA_SCHEDULE_SEGMENTS = 0
+MLA_SCHEDULE_BALANCED = 1
+_SCHEDULES = {"segments": MLA_SCHEDULE_SEGMENTS, "balanced": MLA_SCHEDULE_BALANCED}
+
 HEAD_DIM = 576
 KV_LORA_RANK = 512
 
@@ -82,6 +86,7 @@ class MlaProblem(ctypes.Structure):
         ("q_pe", ctypes.c_void_p),
         ("q_pe_stride_token", ctypes.c_int64),
         ("q_pe_stride_head", ctypes.c_int64),
+        ("schedule", ctypes.c_int32),
     ]
 
 
@@ -208,7 +213,8 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
                  causal: bool = False, q_scale: Optional[torch.Tensor] = None,
                  kv_scale: Optional[torch.Tensor] = None, tile_size: int = 0,
                  num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0,
-                 bt_indptr: Optional[torch.Tensor] = None, q_pe: Optional[torch.Tensor] = None) -> MlaProblem:
+                 bt_indptr: Optional[torch.Tensor] = None, q_pe: Optional[torch.Tensor] = None,
+                 schedule: str = "segments") -> MlaProblem:
     """Fill an ``mla_problem`` from tensors.  Host ints (max_seq_len, max_qlen)
     are passed by the caller so nothing is read back from the device.
 
@@ -218,7 +224,13 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
 
     With ``q_pe`` ([T, H, 64]) q holds only the 512 latent dims ([T, H, 512]):
     the (ql_nope, q_pe) pair of the MLA layer, concatenated in the q load.  A
-    bf16 q with an fp8 cache is quantised in the q load with ``q_scale``."""
+    bf16 q with an fp8 cache is quantised in the q load with ``q_scale``.
+
+    ``schedule`` picks how ``decode`` splits the key axis: "segments" (the
+    segment partition with ``num_segments``, 0 = the planner's S) or
+    "balanced" (equal key ranges per workgroup; ``num_segments`` must be 0)."""
+    if schedule not in _SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(_SCHEDULES)}, got {schedule!r}")
     width = KV_LORA_RANK if q_pe is not None else HEAD_DIM
     if q.ndim != 3 or q.shape[-1] != width or q.stride(-1) != 1:
         raise ValueError(f"q must be [T, H, {width}] with a contiguous last dim, got {tuple(q.shape)}")
@@ -278,6 +290,7 @@ def make_problem(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Ten
     p.tile_size = int(tile_size)
     p.num_segments = int(num_segments)
     p.max_workgroups = int(max_workgroups)
+    p.schedule = _SCHEDULES[schedule]
     return p
 
 
@@ -352,13 +365,15 @@ def decode(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_
            qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
            tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0,
            out_dtype=torch.bfloat16, out=None, lse=None, workspace=None, bt_indptr=None, q_pe=None,
-           stream=None):
-    """Fused decode: returns (out [T, H, 512], lse [T, H])."""
+           schedule: str = "segments", stream=None):
+    """Fused decode: returns (out [T, H, 512], lse [T, H]).  schedule
+    "segments" uses the segment partition (num_segments 0 = the planner's S),
+    "balanced" the balanced split."""
     p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                      max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen, causal=causal,
                      q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
                      num_segments=num_segments, sum_seq_lens=sum_seq_lens, max_workgroups=max_workgroups,
-                     bt_indptr=bt_indptr, q_pe=q_pe)
+                     bt_indptr=bt_indptr, q_pe=q_pe, schedule=schedule)
     T, H = q.shape[0], q.shape[1]
     check_sinks(sinks, H)
     if out is None:
@@ -408,15 +423,16 @@ class Decoder:
                  qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
                  tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0,
                  max_workgroups: int = 0, out_dtype=torch.bfloat16, bt_indptr=None, out=None, lse=None,
-                 q_pe=None):
+                 q_pe=None, schedule: str = "segments"):
         self.p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
                               max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen,
                               causal=causal, q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
                               num_segments=num_segments, sum_seq_lens=sum_seq_lens,
-                              max_workgroups=max_workgroups, bt_indptr=bt_indptr, q_pe=q_pe)
+                              max_workgroups=max_workgroups, bt_indptr=bt_indptr, q_pe=q_pe,
+                              schedule=schedule)
         check_sinks(sinks, q.shape[1])
-        # num_segments == 0 keeps the balanced split (split_workgroups > 0);
-        # otherwise the segment partition with that S.
+        # The balanced split (split_workgroups > 0), or the segment partition
+        # with the resolved S (the planner's when num_segments == 0).
         self.split = split_plan(self.p)
         self.split_workgroups = self.split[0] if self.split else 0
         self.num_segments = 0 if self.split else resolve_num_segments(self.p)

@@ -93,6 +93,13 @@ int validate(const mla_problem* p, bool require_segments) {
                   "tile_size %d must be a power of two <= 128 dividing block_size %d", p->tile_size,
                   p->block_size);
   }
+  if (p->schedule != MLA_SCHEDULE_SEGMENTS && p->schedule != MLA_SCHEDULE_BALANCED)
+    return fail(MLA_ERR_INVALID_ARG, "schedule must be MLA_SCHEDULE_SEGMENTS (0) or MLA_SCHEDULE_BALANCED (1), got %d",
+                p->schedule);
+  if (require_segments && p->schedule != MLA_SCHEDULE_SEGMENTS)
+    return fail(MLA_ERR_INVALID_ARG, "the segment entry points take schedule MLA_SCHEDULE_SEGMENTS (0)");
+  if (p->schedule == MLA_SCHEDULE_BALANCED && p->num_segments != 0)
+    return fail(MLA_ERR_INVALID_ARG, "schedule MLA_SCHEDULE_BALANCED takes num_segments 0, got %d", p->num_segments);
   if (require_segments ? p->num_segments < 1 : p->num_segments < 0)
     return fail(MLA_ERR_INVALID_ARG, "num_segments must be >= %d, got %d", require_segments ? 1 : 0,
                 p->num_segments);
@@ -173,7 +180,7 @@ int plan_segments(int num_reqs, int max_seq_len, int64_t sum_seq_lens, int num_h
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Balanced split of the fused decode (num_segments == 0): the split kernel's
+// Balanced split of the fused decode (MLA_SCHEDULE_BALANCED): the split kernel's
 // shape and workgroup count.  grid_wgs == 0 means "use the segment formula"
 // (the unit count would not fit 32 bits).
 struct SplitPlan {
@@ -363,7 +370,7 @@ int mla_decode_workspace_bytes(const mla_problem* p, size_t* bytes) {
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
   const int st = validate(p, false);
   if (st != MLA_OK) return st;
-  if (p->num_segments == 0) {
+  if (p->schedule == MLA_SCHEDULE_BALANCED) {
     const SplitPlan sp = plan_split(p, resolved_tile(p));
     if (sp.grid_wgs > 0) {
       *bytes = split_ws(sp, p->num_reqs).total;
@@ -380,7 +387,7 @@ int mla_split_plan(const mla_problem* p, int32_t* workgroups, int32_t* rows_per_
                    int32_t* unit_keys) {
   const int st = validate(p, false);
   if (st != MLA_OK) return st;
-  if (p->num_segments != 0) return 0;
+  if (p->schedule != MLA_SCHEDULE_BALANCED) return 0;
   const SplitPlan sp = plan_split(p, resolved_tile(p));
   if (sp.grid_wgs <= 0) return 0;
   if (workgroups) *workgroups = sp.grid_wgs;
@@ -497,7 +504,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
     return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
 
-  if (p->num_segments == 0) {
+  if (p->schedule == MLA_SCHEDULE_BALANCED) {
     const SplitPlan sp = plan_split(p, tile);
     if (sp.grid_wgs > 0) {
       const SplitWs w = split_ws(sp, p->num_reqs);
@@ -527,6 +534,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
         m.seq_lens = p->seq_lens;
         m.qo_indptr = p->qo_indptr;
         m.num_reqs = p->num_reqs;
+        m.max_qlen = p->qo_indptr ? p->max_qlen : 1;
         m.num_tokens = p->num_tokens;
         m.num_heads = p->num_heads;
         m.num_segments = 1;
@@ -572,6 +580,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
     m.seq_lens = p->seq_lens;
     m.qo_indptr = p->qo_indptr;
     m.num_reqs = p->num_reqs;
+    m.max_qlen = p->qo_indptr ? p->max_qlen : 1;
     m.num_tokens = p->num_tokens;
     m.num_heads = p->num_heads;
     m.num_segments = S;

@@ -83,7 +83,7 @@ struct MergeLaunch {
   const int32_t* part_lens;  // [T] or NULL -> derive from seq_lens / qo_indptr
   const int32_t* seq_lens;
   const int32_t* qo_indptr;  // nullable
-  int32_t num_reqs;
+  int32_t num_reqs, max_qlen;
   int32_t num_tokens, num_heads, num_segments, tile;
   const float* sinks;  // nullable
   void* out;

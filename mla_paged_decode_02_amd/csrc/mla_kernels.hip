@@ -51,8 +51,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBufferFlags = 0x00020000;
 // The cache-row stream loads are non-temporal ("nt": each row is read once per
 // piece), which measured ~10% faster than the default policy.
-// The softmax reference max moves only past this many base-2 units (p <= 2^8).
-constexpr float kLazy = 8.0f;
+// The softmax reference max moves only past kLazy base-2 units, and p is
+// taken relative to (reference - kBias), so p <= 2^(kLazy + kBias) = 2^8.
+// bf16 P keeps fp32's range (lazy 8, no bias).  fp8 P is rounded to e4m3,
+// whose smallest step is 2^-9: lazy 6 and a bias of 2 keep p <= 256 < 448
+// while weights down to 2^-12 of the reference stay representable (host
+// simulation on N(0,1) data: under 1% of tiles rescale).
+template <bool FP8>
+struct Lazy {
+  static constexpr float kLazy = FP8 ? 6.0f : 8.0f;
+  static constexpr float kBias = FP8 ? 2.0f : 0.0f;
+};
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -760,11 +769,13 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   };
 
   // Base-2 online softmax per row over one tile.  The reference max m_run
-  // only moves when the tile max exceeds it by more than kLazy (so p <= 2^kLazy);
-  // m_true tracks the exact max and the end rescales to it once.  Returns
-  // whether this lane's rows need the accumulator rescaled by alpha.
+  // only moves when the tile max exceeds it by more than kLazy, and
+  // p = 2^(x - (m_run - kBias)) <= 2^8; m_true tracks the exact max and the
+  // end rescales to it once.  l sums the exact p, lh (fp8) the e4m3-rounded
+  // p the product uses.  Returns whether this lane's rows need the
+  // accumulator rescaled by alpha.
   auto softmax_tile = [&](const SBlk& sblk, int tile_start, float (&m_run)[RG], float (&m_true)[RG],
-                          float (&l_run)[RG], PVal& pv_out, float (&alpha)[RG]) -> bool {
+                          float (&l_run)[RG], float (&lh_run)[RG], PVal& pv_out, float (&alpha)[RG]) -> bool {
     bool rescale = false;
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
@@ -788,31 +799,44 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       }
       mloc = wave_max(mloc);
       m_true[q] = fmaxf(m_true[q], mloc);
-      const float m_new = (mloc > m_run[q] + kLazy) ? mloc : m_run[q];
+      const float m_new = (mloc > m_run[q] + Lazy<FP8>::kLazy) ? mloc : m_run[q];
       alpha[q] = 1.f;
       float pv[4 * kNB];
-      if (m_new == -INFINITY) {
+      const bool live = m_new != -INFINITY;
+      if (!live) {
 #pragma unroll
         for (int i = 0; i < 4 * kNB; ++i) pv[i] = 0.f;
       } else {
         alpha[q] = __builtin_amdgcn_exp2f(m_run[q] - m_new);
-        float psum = 0.f;
+        const float m_ref = m_new - Lazy<FP8>::kBias;
 #pragma unroll
-        for (int i = 0; i < 4 * kNB; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
-          psum += pv[i];
-        }
-        l_run[q] = l_run[q] * alpha[q] + psum;
+        for (int i = 0; i < 4 * kNB; ++i) pv[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
       }
-      m_run[q] = m_new;
-      rescale |= alpha[q] != 1.f;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4 * kNB; ++i) psum += pv[i];
+      if (live) l_run[q] = l_run[q] * alpha[q] + psum;
       if constexpr (FP8) {
-        // P^T in e4m3 for the fp8 P.V product (p <= 2^kLazy = 256 < 448)
+        // P^T in e4m3 for the fp8 P.V product (p <= 2^8 = 256 < 448).
+        // e4m3 flushes p < 2^-10 to zero, so the product's weights can sum
+        // to less than the exact exp-sum l.  lh accumulates the rounded
+        // weights; the end of the piece rescales the accumulator by l / lh,
+        // so the output is the average under the weights the product used
+        // (a constant V stays exact) while l, and with it the LSE, stays the
+        // exact sum.
         int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w0, true);
         int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4], pv[5], 0, false);
         w1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[6], pv[7], w1, true);
         pv_out.pb8[q] = (long)(unsigned)w0 | ((long)(unsigned)w1 << 32);
+        const f32x2 r0 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false), r1 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+        const f32x2 r2 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false), r3 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+        const float hsum = ((r0[0] + r0[1]) + (r1[0] + r1[1])) + ((r2[0] + r2[1]) + (r3[0] + r3[1]));
+        if (live) lh_run[q] = lh_run[q] * alpha[q] + hsum;
+      }
+      m_run[q] = m_new;
+      rescale |= alpha[q] != 1.f;
+      if constexpr (FP8) {
       } else if constexpr (kNB == 2) {
         pv_out.pb[q] = to_bf16x8(pv);
       } else {
@@ -1002,9 +1026,9 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
     for (int q = 0; q < RG; ++q)
 #pragma unroll
       for (int d = 0; d < 32; ++d) acc[q][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[RG], m_true[RG], l_run[RG];
+    float m_run[RG], m_true[RG], l_run[RG], lh_run[RG];
 #pragma unroll
-    for (int q = 0; q < RG; ++q) { m_run[q] = m_true[q] = -INFINITY; l_run[q] = 0.f; }
+    for (int q = 0; q < RG; ++q) { m_run[q] = m_true[q] = -INFINITY; l_run[q] = lh_run[q] = 0.f; }
 
 #pragma unroll
     for (int k = 0; k < NBUF - 1; ++k)
@@ -1035,25 +1059,35 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       qk_tile(buf, qop, qlat, qrope, sblk);
       PVal pvv;
       float alpha[RG];
-      const bool resc = softmax_tile(sblk, seg_start + tile_of(k) * TT, m_run, m_true, l_run, pvv, alpha);
+      const bool resc = softmax_tile(sblk, seg_start + tile_of(k) * TT, m_run, m_true, l_run, lh_run, pvv, alpha);
       if (__ballot(resc)) rescale_acc(acc, alpha);
       __builtin_amdgcn_sched_barrier(0);
       pv_tile(buf, acc, pvv);
     }
 
-    // Final exact-max correction of the lazily rescaled state.
+    // Final exact-max correction of the lazily rescaled state (and, for
+    // fp8, the l / lh weight correction of the e4m3-rounded P).
     float l_tot[RG];
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
-      const float f = (m_true[q] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[q] - m_true[q]);
-      l_run[q] *= f;
+      // p was taken relative to m_run - kBias; rescale to the exact max
+      const float f0 = (m_true[q] == -INFINITY)
+                           ? 1.f
+                           : __builtin_amdgcn_exp2f((m_run[q] - Lazy<FP8>::kBias) - m_true[q]);
+      float f = f0;
+      l_tot[q] = l_run[q] + __shfl_xor(l_run[q], 16);
+      l_tot[q] += __shfl_xor(l_tot[q], 32);
+      if constexpr (FP8) {
+        float lh = lh_run[q] + __shfl_xor(lh_run[q], 16);
+        lh += __shfl_xor(lh, 32);
+        if (lh > 0.f) f *= l_tot[q] / lh;
+      }
+      l_tot[q] *= f0;
 #pragma unroll
       for (int d = 0; d < 32; ++d) {
         acc[q][d] *= f;
         __builtin_amdgcn_sched_barrier(0);
       }
-      l_tot[q] = l_run[q] + __shfl_xor(l_run[q], 16);
-      l_tot[q] += __shfl_xor(l_tot[q], 32);
     }
     bad = __syncthreads_or(bad ? 1 : 0) != 0;
     if constexpr (KS == 1) {
@@ -1116,9 +1150,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
   const int chunk = blockIdx.z;
   int t0 = r, qlen = 1;
   if (p.qo_indptr) {
-    t0 = p.qo_indptr[r];
-    qlen = p.qo_indptr[r + 1] - t0;
-    if (t0 < 0 || qlen < 0 || qlen > p.max_qlen || t0 + qlen > p.num_tokens) return;
+    const int64_t a = p.qo_indptr[r], b = p.qo_indptr[r + 1];
+    if (a < 0 || b < a || b - a > p.max_qlen || b > p.num_tokens) {
+      // Malformed request: the batch tokens its range names get NaN
+      // statistics in this segment's slot (the merge then reports NaN for
+      // them, as for a length past the block table) instead of partials
+      // that were never written.
+      if (chunk == 0) {
+        const int64_t lo = a < 0 ? 0 : a;
+        const int64_t hi = b > p.num_tokens ? p.num_tokens : b;
+        for (int64_t i = lo * p.num_heads + threadIdx.x; i < hi * p.num_heads; i += blockDim.x)
+          p.seg_max[i * p.num_segments + s] = __builtin_nanf("");
+      }
+      return;
+    }
+    t0 = (int)a;
+    qlen = (int)(b - a);
   }
   const int row0 = chunk * kRowsWG;
   if (row0 >= qlen * p.num_heads) return;
@@ -1304,11 +1351,19 @@ void merge_kernel(MergeLaunch p) {
   const int S = p.num_segments;
 
   int req = t;
-  if ((SPLIT || !p.part_lens) && p.qo_indptr) req = request_of_token(p.qo_indptr, p.num_reqs, t);
+  bool malformed = false;
+  if ((SPLIT || !p.part_lens) && p.qo_indptr) {
+    req = request_of_token(p.qo_indptr, p.num_reqs, t);
+    // A request whose query range is malformed gets NaN rows (the stream
+    // kernels computed nothing for it).
+    const int64_t a = p.qo_indptr[req], b = p.qo_indptr[req + 1];
+    malformed = a < 0 || b < a || b - a > p.max_qlen || b > p.num_tokens;
+  }
   int nv = 0;
   const int64_t base = row * S;
   int64_t row_i0 = 0, first_row = 0, stride = 0, gf = 0, W = 1, G = 1;
-  if constexpr (SPLIT) {
+  if (malformed) {
+  } else if constexpr (SPLIT) {
     const int t0 = p.qo_indptr ? p.qo_indptr[req] : req;
     const int qlen = p.qo_indptr ? p.qo_indptr[req + 1] - t0 : 1;
     const int rr = (t - t0) * p.num_heads + h;  // row within the request
@@ -1363,8 +1418,9 @@ void merge_kernel(MergeLaunch p) {
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY, Lsum = 0.f;
-  bool nan_seen = false;
-  if (nv <= 64) {
+  bool nan_seen = malformed;
+  if (malformed) {
+  } else if (nv <= 64) {
     // Common case: statistics of every piece in one load per lane, issued with
     // the first block's data.
     const bool pres = lane < nv && present(lane);

@@ -33,13 +33,14 @@ def vmax(w, reqs=None) -> float:
     return best
 
 
-def run_decode(w, *, num_segments=None, out_dtype=torch.float32, use_indptr=None, sinks=True):
+def run_decode(w, *, num_segments=None, out_dtype=torch.float32, use_indptr=None, sinks=True,
+               schedule="segments"):
     import mla_paged_decode_02_amd as m
     d = mi.to_torch(w, "cuda")
     args = mi.call_args(w, d, use_indptr=use_indptr)
     S = w.num_segments if num_segments is None else num_segments
     out, lse = m.decode(**args, sinks=d["sinks"] if sinks else None, num_segments=S,
-                        out_dtype=out_dtype)
+                        out_dtype=out_dtype, schedule=schedule)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 

@@ -200,7 +200,7 @@ def test_split_q_validates():
 
 # ------------------------------------------------------ balanced split plan --
 
-def _split_problem(H=16, R=4, L=1000, block=16, dtype=torch.bfloat16, qlen=1, **kw):
+def _split_problem(H=16, R=4, L=1000, block=16, dtype=torch.bfloat16, qlen=1, schedule="balanced", **kw):
     T = R * qlen
     q = torch.zeros((T, H, 576), dtype=dtype)
     kv = torch.zeros((R * ((L + block - 1) // block), block, 576), dtype=dtype)
@@ -208,7 +208,7 @@ def _split_problem(H=16, R=4, L=1000, block=16, dtype=torch.bfloat16, qlen=1, **
     sl = torch.full((R,), L, dtype=torch.int32)
     qo = torch.arange(0, T + 1, qlen, dtype=torch.int32) if qlen > 1 else None
     p = m.make_problem(q, kv, bt, sl, softmax_scale=0.1, max_seq_len=L, qo_indptr=qo,
-                       max_qlen=qlen if qlen > 1 else None, sum_seq_lens=R * L, **kw)
+                       max_qlen=qlen if qlen > 1 else None, sum_seq_lens=R * L, schedule=schedule, **kw)
     return p
 
 
@@ -246,10 +246,33 @@ def test_split_plan_aligns_uniform_batches():
 def test_split_plan_respects_max_workgroups_and_segment_mode():
     assert m.split_plan(_split_problem(max_workgroups=3))[0] == 3
     assert m.split_plan(_split_problem(max_workgroups=1))[0] == 1
-    # a fixed segment count uses the segment partition, not the split
-    assert m.split_plan(_split_problem(num_segments=4)) is None
+    # the segment schedule uses the segment partition, not the split, with a
+    # fixed S or with the planner's (num_segments 0)
+    assert m.split_plan(_split_problem(schedule="segments", num_segments=4)) is None
+    p = _split_problem(schedule="segments", R=52, L=16384, block=64)
+    assert m.split_plan(p) is None
+    assert m.resolve_num_segments(p) == m.plan_num_segments(52, 16384, 16, tile_size=64,
+                                                             sum_seq_lens=52 * 16384) == 19
     with pytest.raises(m.MlaError, match="max_workgroups"):
         m.split_plan(_split_problem(max_workgroups=-1))
+
+
+def test_schedule_field_checks():
+    """The balanced split takes no segment count; the segment entry points
+    take only the segment schedule; unknown schedules are rejected."""
+    L = m.lib()
+    p = _split_problem()
+    p.num_segments = 4
+    assert _status(p, require=False) == m.MLA_ERR_INVALID_ARG
+    assert L.mla_decode(ctypes.byref(p), None, 16, 1, 16, None, 0, None) == m.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_segments(ctypes.byref(p), 16, 16, 16, None) == m.MLA_ERR_INVALID_ARG
+    p.schedule = 2
+    p.num_segments = 0
+    assert _status(p, require=False) == m.MLA_ERR_INVALID_ARG
+    p.schedule = m.MLA_SCHEDULE_SEGMENTS
+    assert _status(p, require=False) == m.MLA_OK
+    with pytest.raises(ValueError, match="schedule"):
+        _split_problem(schedule="fixed")
 
 
 def test_split_workspace_covers_two_slots_per_workgroup():
@@ -260,6 +283,7 @@ def test_split_workspace_covers_two_slots_per_workgroup():
     part_rows = g * 2 * rows
     assert need >= part_rows * 512 * 4 + 2 * part_rows * 4 + (5 + 1) * 4
     # the segment partition of the same batch needs [T, H, S, 512] instead
+    p.schedule = m.MLA_SCHEDULE_SEGMENTS
     p.num_segments = 3
     assert m.workspace_bytes(p) >= 5 * 32 * 3 * 512 * 4
 

@@ -76,7 +76,7 @@ def test_dcp_emulation_parity(case, W, shard_dtype):
     outs, lses = [], []
     for sw in mi.dcp_shards(w, W):
         d = mi.to_torch(sw, "cuda")
-        o, l = m.decode(**mi.call_args(sw, d), sinks=None, num_segments=0, out_dtype=shard_dtype)
+        o, l = m.decode(**mi.call_args(sw, d), sinks=None, schedule="balanced", out_dtype=shard_dtype)
         outs.append(o)
         lses.append(l)
     d = mi.to_torch(w, "cuda")

@@ -1,12 +1,14 @@
 """Parity at full size, in the launch configuration the benchmark times.
 
 Each workload is built at its real shape (52 requests x 16384 tokens, the
-128-request ragged causal batch, or 52 index-stream tokens of 2048 rows) and decoded on the GPU with the planner's
-default split through one prepared ``mla_decode`` call, bf16 output (the
-same call ``bench.py`` times).  The fp64 oracle then computes a sample of the
-requests one by one, and the outputs of every token row of those requests are
-compared at the decode tolerances.  The segment partials of the same sample
-are checked too, with the planner's segment count.
+128-request ragged causal batch, or 52 index-stream tokens of 2048 rows) and
+decoded on the GPU with the balanced split through one prepared
+``mla_decode`` call, bf16 output (the call ``bench.py`` times for its
+headline).  The fp64 oracle then computes a sample of the requests one by
+one, and the outputs of every token row of those requests are compared at
+the decode tolerances.  The fused call on the planner's segment partition
+(merged output) and the segment partials of the same sample are checked
+too.
 """
 from __future__ import annotations
 
@@ -22,6 +24,7 @@ pytestmark = pytest.mark.gpu
 
 FULL = {
     "bs52_ctx16k_h16_bf16_blk64": lambda: mi.bs52_h16_bf16(),
+    "bs52_ctx16k_h16_fp8_blk64": lambda: mi.bs52_fp8(16),
     "bs52_ctx16k_h48_fp8_blk64": lambda: mi.bs52_fp8(48),
     "bs52_ctx16k_h64_fp8_blk64": lambda: mi.bs52_fp8(64),
     "bs52_ctx16k_h128_bf16_blk256": lambda: mi.bs52_h128_bf16(),
@@ -59,12 +62,11 @@ def test_fullsize_sampled_parity(name):
     print(f"[fullsize] {name}: T={w.num_tokens} H={w.num_heads} {w.kv_dtype}", flush=True)
     d = mi.to_torch(w, "cuda")
     args = mi.call_args(w, d)
-    dec = m.Decoder(**args, sinks=d["sinks"], num_segments=0, out_dtype=torch.bfloat16)
+    dec = m.Decoder(**args, sinks=d["sinks"], schedule="balanced", out_dtype=torch.bfloat16)
     out, lse = dec.run()
     torch.cuda.synchronize()
-    # The segment partition the planner picks for the same batch (the fused
-    # call itself uses the balanced split when dec.split is set).
-    S = dec.num_segments or m.resolve_num_segments(m.make_problem(**args))
+    # The segment partition the planner picks for the same batch.
+    S = m.resolve_num_segments(m.make_problem(**args))
     out = out.float().cpu().numpy().astype(np.float64)
     lse = lse.cpu().numpy().astype(np.float64)
     assert np.isfinite(out).all()
@@ -76,6 +78,20 @@ def test_fullsize_sampled_parity(name):
     err_o, err_l = assert_close(w, out, lse, ref_o, ref_l, reqs=reqs, tok=tok)
     print(f"[fullsize] {name}: split={dec.split} S={S} reqs={reqs} max|dO|={err_o:.3e} "
           f"max|dLSE|={err_l:.3e}", flush=True)
+    del out, lse
+
+    # The fused call on the planner's segment partition: merged output of the
+    # same sample.
+    dseg = m.Decoder(**args, sinks=d["sinks"], num_segments=0, out_dtype=torch.bfloat16)
+    assert dseg.split is None and dseg.num_segments == S
+    out_s, lse_s = dseg.run()
+    torch.cuda.synchronize()
+    out_s = out_s.float().cpu().numpy().astype(np.float64)
+    lse_s = lse_s.cpu().numpy().astype(np.float64)
+    assert np.isfinite(out_s).all()
+    err_o, err_l = assert_close(w, out_s, lse_s, ref_o, ref_l, reqs=reqs, tok=tok)
+    print(f"[fullsize] {name}: segments S={S} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+    del out_s, lse_s, dseg
 
     # Segment partials of the same sample, same segment count and tile.
     tile = w.tile_size or m.tile_size_for_block(w.block_size)

@@ -172,15 +172,17 @@ def test_parity_sweep(case):
     assert_close(w, out, lse, ref_o, ref_l)
 
 
-def test_planner_choice_and_empty_requests():
-    """num_segments = 0 (planner) and requests of length 0, with sinks."""
+@pytest.mark.parametrize("schedule", ["segments", "balanced"])
+def test_planner_choice_and_empty_requests(schedule):
+    """num_segments = 0 (the planner's S, or the balanced split) and requests
+    of length 0, with sinks."""
     w = mi.make_workload(name="empty", seq_lens=[0, 500, 0, 64], num_heads=16, block_size=64,
                          dtype="bf16", sinks=True, seed=31)
     ref_o, ref_l = orc.mla_decode(w)
-    out, lse = run_decode(w, num_segments=0)
+    out, lse = run_decode(w, num_segments=0, schedule=schedule)
     assert_close(w, out, lse, ref_o, ref_l)
     assert np.all(out[0] == 0) and np.allclose(lse[0], w.sinks, atol=0, rtol=0)
-    out2, lse2 = run_decode(w, num_segments=0, sinks=False)
+    out2, lse2 = run_decode(w, num_segments=0, sinks=False, schedule=schedule)
     assert np.all(out2[0] == 0) and np.all(np.isneginf(lse2[0]))
 
 
@@ -246,8 +248,8 @@ def test_prepared_decoder_matches_decode():
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-# ------------------------------------------------- balanced split (S = 0) ----
-# mla_decode with num_segments == 0 cuts the batch's units (request, row chunk,
+# ------------------------------------------------------- balanced split ----
+# mla_decode with schedule "balanced" cuts the batch's units (request, row chunk,
 # tile) into equal workgroup ranges.  max_workgroups forces few workgroups so
 # that ranges hold several whole requests, start or end inside one, or lie
 # inside one; the default uses every slot of the device.
@@ -264,7 +266,7 @@ def test_split_parity_sweep(case, wgs):
     ref_o, ref_l = orc.mla_decode(w)
     d = mi.to_torch(w, "cuda")
     args = mi.call_args(w, d)
-    out, lse = m.decode(**args, sinks=d["sinks"], num_segments=0, max_workgroups=wgs,
+    out, lse = m.decode(**args, sinks=d["sinks"], schedule="balanced", max_workgroups=wgs,
                         out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert_close(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
@@ -283,9 +285,9 @@ def test_split_long_row_among_short_ones(dtype):
                          sinks=True, seed=77 if dtype == "bf16" else 78)
     d = mi.to_torch(w, "cuda")
     args = mi.call_args(w, d)
-    out, lse = m.decode(**args, sinks=d["sinks"], num_segments=0, out_dtype=torch.float32)
+    out, lse = m.decode(**args, sinks=d["sinks"], schedule="balanced", out_dtype=torch.float32)
     torch.cuda.synchronize()
-    g, rows_wg, tt = m.split_plan(m.make_problem(**args, num_segments=0))
+    g, rows_wg, tt = m.split_plan(m.make_problem(**args, schedule="balanced"))
     assert (40000 // tt) * g // (sum(-(-n // tt) for n in lens)) > 64  # the long row's pieces
     ref_o, ref_l = orc.mla_decode(w, reqs=[0, 59, 60])
     sel = [0, 59, 60]
@@ -317,7 +319,8 @@ def test_split_counts_every_key_once(dtype, wgs):
             flat[row, :14] = [one * x for x in bits]
     w = mi.with_(w, kv_scale=None if dtype == "bf16" else 1.0, q_scale=None if dtype == "bf16" else 1.0)
     d = mi.to_torch(w, "cuda")
-    out, lse = m.decode(**mi.call_args(w, d), num_segments=0, max_workgroups=wgs, out_dtype=torch.float32)
+    out, lse = m.decode(**mi.call_args(w, d), schedule="balanced", max_workgroups=wgs,
+                        out_dtype=torch.float32)
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     qo = w.qo_indptr
@@ -341,8 +344,8 @@ def test_split_stages_and_decoder():
                          dtype="fp8_e4m3", sinks=True, seed=101)
     d = mi.to_torch(w, "cuda")
     args = mi.call_args(w, d)
-    o1, l1 = m.decode(**args, sinks=d["sinks"], num_segments=0)
-    dec = m.Decoder(**args, sinks=d["sinks"], num_segments=0)
+    o1, l1 = m.decode(**args, sinks=d["sinks"], schedule="balanced")
+    dec = m.Decoder(**args, sinks=d["sinks"], schedule="balanced")
     assert dec.split_workgroups > 0 and dec.num_segments == 0
     for _ in range(3):
         dec.run_stage(1)

@@ -35,16 +35,18 @@ PAGED = [
 
 
 def _run(w, S, wgs=0):
+    """S None: the balanced split (at most wgs workgroups, 0 = all slots);
+    else the segment partition (0 = the planner's S)."""
     import mla_paged_decode_02_amd as m
     d = mi.to_torch(w, "cuda")
-    out, lse = m.decode(**mi.call_args(w, d), sinks=d["sinks"], num_segments=S, max_workgroups=wgs,
-                        out_dtype=torch.float32)
+    sched = dict(schedule="balanced", max_workgroups=wgs) if S is None else dict(num_segments=S)
+    out, lse = m.decode(**mi.call_args(w, d), sinks=d["sinks"], **sched, out_dtype=torch.float32)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
 @pytest.mark.parametrize("case", PAGED, ids=lambda c: f"{c[0]}-H{c[1]}-blk{c[2]}-q{c[4] is not None}")
-@pytest.mark.parametrize("S,wgs", [(0, 0), (0, 3), (3, 0)])
+@pytest.mark.parametrize("S,wgs", [(None, 0), (None, 3), (0, 0), (3, 0)])
 def test_ragged_page_lists_match_table(case, S, wgs):
     dtype, H, block, lens, qlens, causal, sinks = case
     _print_case(f"ragged-pages S={S} wgs={wgs} {case}")
@@ -71,7 +73,7 @@ SPARSE = [
 
 
 @pytest.mark.parametrize("case", SPARSE, ids=lambda c: f"{c[0]}-H{c[1]}-n{len(c[2])}")
-@pytest.mark.parametrize("S,wgs", [(0, 0), (0, 2), (2, 0)])
+@pytest.mark.parametrize("S,wgs", [(None, 0), (None, 2), (0, 0), (2, 0)])
 def test_sparse_index_stream_parity(case, S, wgs):
     dtype, H, counts, ctx = case
     _print_case(f"sparse S={S} wgs={wgs} {case}")
