@@ -256,6 +256,24 @@ int mla_decode(const mla_problem* p, const float* sinks, void* out, int32_t out_
 int mla_decode_stage(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
                      void* workspace, size_t workspace_bytes, int32_t stage, void* stream);
 
+/*
+ * mla_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, serving loops that must not call
+ * the allocator, harnesses that forbid it).  The partials live in a static
+ * device array of MLA_NO_ALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; nothing is allocated or freed.  The
+ * caller still passes q, the cache and the outputs.  160 MiB holds the
+ * balanced split's partials for any batch on a 256-CU MI355X (at most
+ * 32768 rows x 2 pieces x 2056 B); a segment partition needs
+ * T * H * S * 2056 B.  A batch whose mla_decode_workspace_bytes exceeds the
+ * scratch size fails with MLA_ERR_WORKSPACE before any launch.  All calls on one GPU share the one
+ * array: calls that overlap on a GPU (concurrent streams, threads) race and
+ * must be ordered by the caller.  Other arguments as for mla_decode.
+ */
+#define MLA_NO_ALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+int mla_decode_no_alloc(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
+                        void* stream);
+
 /* Workspace mla_decode needs for p.  Returns 0 and sets *bytes, or an error. */
 int mla_decode_workspace_bytes(const mla_problem* p, size_t* bytes);
 

@@ -96,8 +96,11 @@ EXPORTED = (
     "mla_validate", "mla_decode_segments", "mla_merge_segments", "mla_decode",
     "mla_decode_workspace_bytes", "mla_resolve_num_segments", "mla_plan_num_segments",
     "mla_tile_size_for_block", "mla_segment_bounds", "mla_status_string", "mla_last_error",
-    "mla_version", "mla_decode_stage", "mla_split_plan", "mla_combine_lse",
+    "mla_version", "mla_decode_stage", "mla_split_plan", "mla_combine_lse", "mla_decode_no_alloc",
 )
+
+# Size of the library's static device scratch (mla_decode_no_alloc).
+NO_ALLOC_SCRATCH_BYTES = 160 << 20
 
 
 def lib() -> ctypes.CDLL:
@@ -115,6 +118,7 @@ def lib() -> ctypes.CDLL:
     L.mla_merge_segments.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp]
     L.mla_decode.argtypes = [P, vp, vp, i32, vp, vp, sz, vp]
     L.mla_decode_stage.argtypes = [P, vp, vp, i32, vp, vp, sz, i32, vp]
+    L.mla_decode_no_alloc.argtypes = [P, vp, vp, i32, vp, vp]
     L.mla_combine_lse.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, i32, vp, vp]
     L.mla_split_plan.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.mla_decode_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
@@ -130,7 +134,7 @@ def lib() -> ctypes.CDLL:
     for f in ("mla_validate", "mla_decode_segments", "mla_merge_segments", "mla_decode",
               "mla_decode_workspace_bytes", "mla_resolve_num_segments", "mla_plan_num_segments",
               "mla_tile_size_for_block", "mla_segment_bounds", "mla_version", "mla_decode_stage",
-              "mla_split_plan", "mla_combine_lse"):
+              "mla_split_plan", "mla_combine_lse", "mla_decode_no_alloc"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -386,6 +390,25 @@ def decode(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_
     _check(lib().mla_decode(ctypes.byref(p), _ptr(sinks), _ptr(out), _out_code(out.dtype), _ptr(lse),
                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _stream(stream)))
+    return out, lse
+
+
+def decode_no_alloc(q, kv_cache, block_table, seq_lens, *, softmax_scale: float, max_seq_len: int, out, lse,
+                    qo_indptr=None, max_qlen=None, causal=False, q_scale=None, kv_scale=None, sinks=None,
+                    tile_size: int = 0, num_segments: int = 0, sum_seq_lens: int = 0, max_workgroups: int = 0,
+                    bt_indptr=None, q_pe=None, schedule: str = "segments", stream=None):
+    """mla_decode_no_alloc: the fused decode with the library's static device
+    scratch instead of a workspace (out [T, H, 512] and lse [T, H] are given
+    by the caller; nothing is allocated).  Calls on one GPU share the scratch
+    and must not overlap."""
+    p = make_problem(q, kv_cache, block_table, seq_lens, softmax_scale=softmax_scale,
+                     max_seq_len=max_seq_len, qo_indptr=qo_indptr, max_qlen=max_qlen, causal=causal,
+                     q_scale=q_scale, kv_scale=kv_scale, tile_size=tile_size,
+                     num_segments=num_segments, sum_seq_lens=sum_seq_lens, max_workgroups=max_workgroups,
+                     bt_indptr=bt_indptr, q_pe=q_pe, schedule=schedule)
+    check_sinks(sinks, q.shape[1])
+    _check(lib().mla_decode_no_alloc(ctypes.byref(p), _ptr(sinks), _ptr(out), _out_code(out.dtype), _ptr(lse),
+                                     _stream(stream)))
     return out, lse
 
 

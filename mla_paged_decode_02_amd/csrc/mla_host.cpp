@@ -16,6 +16,8 @@
 #include "mla_decode.h"
 #include "mla_internal.h"
 
+static_assert(mla::kScratchBytes == MLA_NO_ALLOC_SCRATCH_BYTES, "static scratch size of the header");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -600,6 +602,21 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
 int mla_decode(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
                void* workspace, size_t workspace_bytes, void* stream) {
   return decode_stages(p, sinks, out, out_dtype, lse, workspace, workspace_bytes, 3, stream);
+}
+
+int mla_decode_no_alloc(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
+                        void* stream) {
+  size_t need = 0;
+  int st = mla_decode_workspace_bytes(p, &need);
+  if (st != MLA_OK) return st;
+  if (need > mla::kScratchBytes)
+    return fail(MLA_ERR_WORKSPACE, "mla_decode_no_alloc: the batch needs %zu bytes of scratch; the static scratch holds %zu",
+                need, mla::kScratchBytes);
+  if (p->num_tokens == 0) return decode_stages(p, sinks, out, out_dtype, lse, nullptr, 0, 3, stream);
+  void* ws = nullptr;
+  hipError_t e = mla::scratch_buffer(&ws);
+  if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  return decode_stages(p, sinks, out, out_dtype, lse, ws, mla::kScratchBytes, 3, stream);
 }
 
 int mla_decode_stage(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,

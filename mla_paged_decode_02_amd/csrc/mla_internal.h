@@ -132,4 +132,9 @@ hipError_t launch_segments(const SegmentLaunch& a, const SegmentShape& sh, int s
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream);
 
+// The library's static device scratch (mla_decode_no_alloc): its size, and
+// its device address on the current device.
+constexpr size_t kScratchBytes = (size_t)160 << 20;
+hipError_t scratch_buffer(void** ptr);
+
 }  // namespace mla

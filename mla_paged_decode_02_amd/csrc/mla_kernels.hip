@@ -27,7 +27,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "mla_internal.h"
 
@@ -1664,7 +1666,32 @@ hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, int 
   }
 }
 
+// Scratch for callers that cannot allocate (mla_decode_no_alloc): the fused
+// decode's partials and unit offsets.  Every GPU holds its own copy until
+// the process ends; calls that overlap on one GPU share it and race.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 }  // namespace
+
+hipError_t scratch_buffer(void** ptr) {
+  // The device address of `scratch` on the current device, looked up once per
+  // device (the host-side name of the array is not a device address).
+  static std::mutex mu;
+  static std::vector<void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
   SegmentShape sh;

@@ -295,3 +295,15 @@ def test_decode_stage_rejects_bad_stage_before_launch():
     assert L.mla_decode_stage(ctypes.byref(p), None, 16, 1, 16, None, 0, 0, None) == m.MLA_ERR_INVALID_ARG
     # a valid stage with no workspace fails on the workspace, still before any launch
     assert L.mla_decode_stage(ctypes.byref(p), None, 16, 1, 16, None, 0, 1, None) == m.MLA_ERR_WORKSPACE
+
+
+def test_no_alloc_rejects_batches_beyond_the_scratch_before_launch():
+    """mla_decode_no_alloc refuses a batch whose partials exceed the static
+    scratch (MLA_ERR_WORKSPACE, no launch, no device call)."""
+    L = m.lib()
+    p = _split_problem(H=128, R=52, L=16384, block=256, schedule="segments", num_segments=20)
+    assert m.workspace_bytes(p) > m.NO_ALLOC_SCRATCH_BYTES
+    assert L.mla_decode_no_alloc(ctypes.byref(p), None, 16, 1, 16, None) == m.MLA_ERR_WORKSPACE
+    assert "static scratch" in L.mla_last_error().decode()
+    p.num_heads = 200
+    assert L.mla_decode_no_alloc(ctypes.byref(p), None, 16, 1, 16, None) == m.MLA_ERR_UNSUPPORTED
