@@ -209,7 +209,7 @@ def time_schedule(w, ds, calls, schedule, args, torch, m, stream):
            "stream_kernel_us": round(stage_us[1], 2), "merge_kernel_us": round(stage_us[2], 2)}
     if decs[0].split is not None:
         sched = split_schedule(w, *decs[0].split)
-        alg = kv_bytes + q_bytes + sched["final_rows"] * (512 * 2 + 4) + sched["partial_rows"] * (512 + 2) * 4
+        alg = kv_bytes + q_bytes + sched["final_rows"] * (512 * 2 + 4) + sched["partial_rows"] * (512 * 2 + 8)
         kernel = "split_kernel"
         res["split"] = {"workgroups": decs[0].split[0], "rows_per_workgroup": decs[0].split[1],
                         "unit_keys": decs[0].split[2], **sched}

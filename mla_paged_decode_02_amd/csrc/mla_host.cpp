@@ -238,7 +238,7 @@ SplitWs split_ws(const SplitPlan& sp, int num_reqs) {
   SplitWs w;
   const size_t rows = (size_t)sp.grid_wgs * 2 * sp.rows_wg;
   w.out_off = 0;
-  w.max_off = align256(rows * MLA_KV_LORA_RANK * sizeof(float));
+  w.max_off = align256(rows * MLA_KV_LORA_RANK * sizeof(float));  // fp32 (or bf16) piece partials
   w.sum_off = w.max_off + align256(rows * sizeof(float));
   w.off_off = w.sum_off + align256(rows * sizeof(float));
   w.total = w.off_off + align256((size_t)(num_reqs + 1) * sizeof(int32_t));
@@ -513,12 +513,15 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
       if (!workspace || workspace_bytes < w.total)
         return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                     workspace ? workspace_bytes : (size_t)0);
+      // piece partials: fp32 for fp32 outputs, else bf16 in the same region
       float* so = reinterpret_cast<float*>(ws + w.out_off);
+      uint16_t* po = reinterpret_cast<uint16_t*>(ws + w.out_off);
       float* sm = reinterpret_cast<float*>(ws + w.max_off);
       float* ss = reinterpret_cast<float*>(ws + w.sum_off);
       int32_t* offs = reinterpret_cast<int32_t*>(ws + w.off_off);
       if (stages & 1) {
         mla::SegmentLaunch a = make_launch(p, tile, 1, so, sm, ss);
+        a.piece_out = po;
         a.out = out;
         a.out_dtype = oc;
         a.lse = lse;
@@ -531,6 +534,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
         mla::MergeLaunch m;
         memset(&m, 0, sizeof(m));
         m.seg_out = so;
+        m.piece_out = po;
         m.seg_max = sm;
         m.seg_sum = ss;
         m.seq_lens = p->seq_lens;

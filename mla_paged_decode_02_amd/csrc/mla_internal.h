@@ -27,8 +27,10 @@ constexpr ShapeCfg shape_cfg(bool fp8, int waves, int rg) {
   // Four waves: two workgroups per CU (two waves per SIMD hide each other's
   // LDS and MFMA latency; measured 1.9x faster than one 144 KiB workgroup).
   // Eight waves: one workgroup, two waves per SIMD.
-  // Two row groups per wave: every LDS read feeds two MFMAs; one wave per SIMD.
-  return rg == 2 ? (waves == 2 ? ShapeCfg{32, 73728, 1} : ShapeCfg{32, 147456, 1})
+  // Two row groups per wave (the wide fp8 body, 32 rows per wave): one wave
+  // per SIMD, rings of 2, 4 or 8 32-token tiles (4, 2 or 1 workgroups per CU).
+  return rg == 2 ? (waves == 1 ? ShapeCfg{32, 36864, 1}
+                    : waves == 2 ? ShapeCfg{32, 73728, 1} : ShapeCfg{32, 147456, 1})
        : waves == 1 ? ShapeCfg{fp8 ? 32 : 16, 36864, 1}
        : waves == 2 ? ShapeCfg{32, 73728, 1}
        : waves == 4 ? ShapeCfg{fp8 ? 32 : 16, 73728, 2}
@@ -64,8 +66,11 @@ struct SegmentLaunch {
   int32_t num_tokens, num_heads, num_reqs, max_qlen;
   int32_t causal, tile, num_segments;
   float softmax_scale;
-  // partial outputs (segment partials, or the split kernel's piece partials)
+  // partial outputs: segment partials (fp32 seg_out), or the split kernel's
+  // piece partials (fp32 at seg_out when out_dtype is fp32, else bf16 at
+  // piece_out, the same memory); seg_max / seg_sum for both
   float* seg_out;
+  unsigned short* piece_out;
   float* seg_max;
   float* seg_sum;
   // split kernel: finished rows go straight to the output
@@ -77,7 +82,8 @@ struct SegmentLaunch {
 };
 
 struct MergeLaunch {
-  const float* seg_out;
+  const float* seg_out;             // segment partials, and split pieces for fp32 outputs
+  const unsigned short* piece_out;  // split pieces for 16-bit outputs (bf16)
   const float* seg_max;
   const float* seg_sum;
   const int32_t* part_lens;  // [T] or NULL -> derive from seq_lens / qo_indptr
@@ -110,7 +116,7 @@ struct CombineLaunch {
 struct SegmentShape {
   bool fp8;
   int waves;          // waves per workgroup (1, 2, 4 or 8)
-  int rows_per_wave;  // 16-row groups per wave
+  int rows_per_wave;  // 16-row groups per wave (2: the wide fp8 body, one 32-row block)
   int chunks;         // row chunks per (request, segment)
   bool contig;        // TILE >= tile tokens: an LDS tile is one contiguous run of rows
   int ks;             // balanced split: k-split waves per workgroup (1 = none)

@@ -960,12 +960,20 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         stat1 = 0.f;
         stat1_p = nullptr;
       } else {
+        // segment partials in fp32; the balanced split's piece partials in
+        // fp32 for fp32 outputs, else in bf16 (a rounding of the size the
+        // 16-bit output takes anyway)
         const int64_t slot = pc.mode == kOutSegment
                                  ? ((int64_t)(t0 + ti[q]) * H + hh[q]) * p.num_segments + pc.s
                                  : pc.prow0 + (rgw * RG + q) * 16 + n;
         mult = ks;
-        kind = 2;
-        dst = (char*)(p.seg_out + slot * kKvRank + 16 * db0 + 4 * g);
+        if (pc.mode == kOutSegment || p.out_dtype == 2) {
+          kind = 2;
+          dst = (char*)(p.seg_out + slot * kKvRank + 16 * db0 + 4 * g);
+        } else {
+          kind = 0;
+          dst = (char*)(p.piece_out + slot * kKvRank + 16 * db0 + 4 * g);
+        }
         stat0 = bad_all ? __builtin_nanf("") : m_fin[q];
         stat0_p = p.seg_max + slot;
         stat1 = l_tot;
@@ -1137,6 +1145,625 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide waves (fp8): 32 query rows per wave
+// ---------------------------------------------------------------------------
+// A wave owns 32 rows (token, head) and works on 32x32 blocks:
+//   S^T[token, row] = K . Q^T     v_mfma_scale_f32_32x32x64_f8f6f4: 8 latent
+//                                 steps of 64 dims + 1 rope step per tile
+//   O^T[dim, row]  += V^T . P^T   v_mfma_f32_32x32x16_fp8: 16 blocks of 32
+//                                 dims x 2 steps of 16 tokens per tile
+// Every K or V byte a wave reads from LDS feeds 32 rows (the 16-row shapes
+// feed 16), and the accumulator (512 dims x 32 rows: 256 registers per lane)
+// fits the AGPRs at one wave per SIMD.  The LDS tile keeps the regions of
+// KvFmt<true> (V rows of 512 B, rope rows of 64 B at +16 KiB) with its own V
+// swizzle, swz_w.
+//
+// Lane layouts (checked on gfx950 with a lane probe):
+//  32x32x64 f8f6f4: A lane l = row l%32, k 32(l/32)..+31; B lane l = column
+//    l%32, k 32(l/32)..+31; D lane l, register r = row 8(r/4)+4(l/32)+r%4,
+//    column l%32.  32x32x16 fp8: the same with k 8(l/32)..+7.
+//  ds_read_b64_tr_b8: each lane of a 16-lane group reads 8 bytes (row
+//    lane/2 of an 8 x 16-byte block, half lane%2); lane n of the group gets
+//    byte n of the block's rows 0..7.
+// So the S^T accumulator (tokens 8(r/4)+4(l/32)+r%4 of column l%32) is the
+// P^T operand of the two 16-token steps as it stands (registers 8s..8s+7 for
+// step s), and the V^T reads fetch the same token order.
+
+// Chunk swizzle of the wide tile's V region (16-byte chunk c of row r sits at
+// c ^ swz_w(r)): a bijection of r's low four bits, so the 16 rows one K read
+// serves at once land in 16 distinct bank groups; its bits 3..1 are a
+// bijection of (r1, r0, r3), so the 8 rows of a transpose-read group (r2
+// fixed) land in 8 distinct 32-byte bank pairs.
+__device__ __forceinline__ int swz_w(int r) {
+  return (((r >> 1) & 1) << 3) | ((r & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// One step of S^T = K . Q^T (64 dims, e4m3 x e4m3): v_mfma_f32_32x32x64_f8f6f4
+// written with its result in VGPRs.  At one wave per SIMD the compiler gives
+// every MFMA it emits an AGPR result, and the 512-dim accumulator already
+// takes all 256 AGPRs.  The steps of one tile chain through the same
+// registers (exact overlap of the accumulator needs no wait states); the
+// last step ends with the wait states a VALU read of its result needs
+// (24 >= the compiler's own for this MFMA), so the result may be read by any
+// instruction after it.  Each step opens with the 2 wait states an MFMA
+// operand written by a VALU instruction needs.
+template <bool FIRST, bool LAST>
+__device__ __forceinline__ void qk_step_w32(f32x16& s, const i32x8& k, const i32x8& q) {
+  if constexpr (FIRST && LAST) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0\n\ts_nop 15\n\ts_nop 7"
+                 : "=&v"(s) : "v"(k), "v"(q));
+  } else if constexpr (FIRST) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "v"(q));
+  } else if constexpr (LAST) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 7"
+                 : "+v"(s) : "v"(k), "v"(q));
+  } else {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
+  }
+}
+
+// One P.V step O^T += 2^e V^T . P^T (64 tokens, e4m3, E8M0 scale 2^e of the
+// P^T columns, V^T unscaled), v_mfma_scale_f32_32x32x64_f8f6f4 on an AGPR
+// accumulator, written as assembly so that it keeps its place among the DMA
+// and LDS instructions the stream puts between the steps.  It opens with the
+// 2 wait states an operand written by a VALU instruction needs; an
+// accumulator chained from the previous step on the same registers needs
+// none.  mfma_settle_w32 gives the wait states a read of the last result
+// needs.
+__device__ __forceinline__ void pv_step_w32(f32x16& acc, const i32x8& v, const i32x8& pt, int scale_a,
+                                            int scale_b) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+a"(acc)
+               : "v"(v), "v"(pt), "v"(scale_a), "v"(scale_b));
+}
+__device__ __forceinline__ void mfma_settle_w32() { asm volatile("s_nop 15\n\ts_nop 7"); }
+
+template <int NW, int NBUF, bool QB>
+__device__ __forceinline__ void run_piece_w32(const SegmentLaunch& p, char (*lds)[18432], unsigned lds_u32,
+                                              const Piece& pc) {
+  constexpr int TT = 32;                        // tokens per DMA tile (ring slot)
+  constexpr int kRowBytes = 576;
+  constexpr int kTileBytes = TT * kRowBytes;
+  constexpr int kVRegion = TT * 512;
+  constexpr int kRowsWG = 32 * NW;
+  constexpr int kNI = 18;                       // DMA instructions per tile: 16 V (2 rows) + 2 rope (16 rows)
+  constexpr int kNIw = kNI / NW;                // per wave, lower bound
+  constexpr int kVw = 16 / NW;                  // V instructions per wave
+  static_assert(kTileBytes == 18432, "fp8 32-token tiles");
+  static_assert(NW == 2 || NW == 4, "the wide body runs two or four waves");
+  static_assert(NBUF >= 3, "a tile in the P.V phase, one in the QK phase, and one in flight");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 31;  // the lane's query row in the wave
+  const int h = lane >> 5;
+
+  const int r = pc.r, t0 = pc.t0, qlen = pc.qlen, L = pc.L;
+  const int H = p.num_heads;
+  const int M = qlen * H;
+  const int row0 = pc.row0;
+  int64_t bt_base;
+  int cap;
+  page_list(p, r, &bt_base, &cap);
+  bt_base = __builtin_amdgcn_readfirstlane((int)(bt_base & 0xffffffff)) |
+            ((int64_t)__builtin_amdgcn_readfirstlane((int)(bt_base >> 32)) << 32);
+  cap = __builtin_amdgcn_readfirstlane(cap);
+  bool bad = L > cap;
+  const int seg_start = pc.seg_start;
+  const int seg_end = pc.seg_end;
+  const int last_row = min(row0 + kRowsWG, M) - 1;
+  const int lim_wg = p.causal ? (L - qlen + last_row / H + 1) : L;
+  const int eff_end = min(min(seg_end, lim_wg), cap);
+  const int ntiles = eff_end > seg_start ? cdiv(eff_end - seg_start, TT) : 0;
+
+  // The lane's query row (lanes l and l + 32 hold the same row).
+  const int row = row0 + wave * 32 + j;
+  const bool rok = row < M;
+  const int ti = rok ? row / H : 0;
+  const int hh = rok ? row - ti * H : 0;
+  const int lim = rok ? (p.causal ? max(0, L - qlen + ti + 1) : L) : 0;
+  const int end_row = min(seg_end, lim);
+  int end_min;  // keys every valid row of the wave sees: steps below need no mask
+  {
+    int v = rok ? end_row : 0x7fffffff;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = min(v, __shfl_xor(v, off));
+    end_min = min(__builtin_amdgcn_readfirstlane(v), eff_end);
+  }
+
+  const float qs = p.q_scale ? *p.q_scale : 1.0f;
+  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
+  const float sl2 = p.softmax_scale * kLog2e * qs * ks;
+
+  // ---- Q^T operand: lane (j, h) holds row j's dims 64c + 32h .. +31 (c = 8: rope) ----
+  i32x8 qop[9];
+  {
+    const int64_t tok = t0 + ti;
+    const int64_t qoff = tok * p.q_stride_token + (int64_t)hh * p.q_stride_head;
+    const int64_t poff = p.q_pe ? tok * p.q_pe_stride_token + (int64_t)hh * p.q_pe_stride_head : qoff + kKvRank;
+    if constexpr (!QB) {
+      const uint8_t* qb = (const uint8_t*)p.q + qoff;
+      const uint8_t* qr = (const uint8_t*)(p.q_pe ? p.q_pe : p.q) + poff;
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        const uint8_t* src = c < 8 ? qb + 64 * c + 32 * h : qr + 32 * h;
+        const u32x4 lo = rok ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
+        const u32x4 hi = rok ? *(const u32x4*)(src + 16) : u32x4{0, 0, 0, 0};
+        qop[c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    } else {
+      // bf16 q quantised here: code = e4m3 RNE of sat(q / q_scale)
+      const unsigned short* qb = (const unsigned short*)p.q + qoff;
+      const unsigned short* qr = (const unsigned short*)(p.q_pe ? p.q_pe : p.q) + poff;
+      auto quant8 = [&](const unsigned short* src) -> u32x2 {
+        const u32x4 v = rok ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = __uint_as_float(v[i] << 16);
+          f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float y = __fdiv_rn(f[i], qs);
+          f[i] = y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
+        }
+        u32x2 o;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * k], f[4 * k + 1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * k + 2], f[4 * k + 3], w, true);
+          o[k] = (unsigned)w;
+        }
+        return o;
+      };
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        const unsigned short* src = c < 8 ? qb + 64 * c + 32 * h : qr + 32 * h;
+        i32x8 x;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x2 w = quant8(src + 8 * k);
+          x[2 * k] = (int)w[0];
+          x[2 * k + 1] = (int)w[1];
+        }
+        qop[c] = x;
+      }
+    }
+  }
+
+  // ---- DMA of one tile into ring slot b ----
+  // Instruction i < kVw of wave w fills V rows 2m and 2m + 1, m = kVw w + i
+  // (lanes 0-31 row 2m, lanes 32-63 row 2m + 1): lane l writes physical
+  // chunk l % 32 and loads the logical chunk the swizzle puts there.  With
+  // r = 2m + hb, chunk c ^ swz_w(r) = (c ^ 4 hb) ^ g(m) for the scalar
+  // g(m) = 8 (m & 1) | 2 ((m >> 2) & 1) | ((m >> 1) & 1), so a lane's offset
+  // is its fixed part u_v (XOR) the scalar 16 g(m), plus its row part h_v,
+  // with the scalar row offset 1152 m in soffset.  Instruction kVw of waves
+  // 0 and 1 fills rope rows 16w .. 16w + 15 (4 lanes per 64-byte row, chunk
+  // c at c ^ ((row / 4) % 4)): the lane part r_v plus the scalar 9216 w.
+  // The buffer descriptor covers the tile's valid rows only, so rows at or
+  // past the valid count read as zeros (finite data the softmax masks) and a
+  // tile past the piece's end (every offset out of range) fetches nothing.
+  // tile_setup resolves the tile's page through a scalar cursor over the
+  // page table (its scalar load is waited for there, before any LDS read is
+  // in flight); dma_ins issues one of the wave's instructions, so the stream
+  // spreads them over the P.V MFMAs.
+  constexpr int kNDw = kVw + 1;  // instruction slots per wave (the rope one is empty for waves 2 and 3)
+  constexpr int kNIo = kVw + (NW == 2 ? 1 : 0);  // instructions per tile of waves 2 and 3 (NW 2: of all)
+  const int hb = lane >> 5;
+  const int u_v = 16 * ((lane & 31) ^ (4 * hb));
+  const int h_v = hb * kRowBytes;
+  const int r_v = (lane >> 2) * kRowBytes + kKvRank + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+  int cur_start = -1, cur_blk_i = 0, cur_in = 0, cached_blk_i = -1;
+  int64_t cached_off = 0;
+  // The next page's table entry is loaded when a page is entered, so the
+  // scalar load is long back when the stream reaches that page.
+  int pf_i = -1, pf_blk = 0;
+  const int npages_tab = cap / p.block_size;
+  auto table_entry = [&](int i) {
+    return ((const __attribute__((address_space(4))) int*)p.block_table)[bt_base + (int64_t)i * p.bt_stride_col];
+  };
+  i32x4 t_rsrc;
+  unsigned t_lbase = 0;
+  auto tile_setup = [&](int k, int b) {
+    t_lbase = lds_u32 + (unsigned)(b * kTileBytes);
+    if (k >= ntiles) {
+      t_rsrc = make_rsrc(p.kv, 0);  // past the piece: fetches nothing
+      return;
+    }
+    const int tile_start = seg_start + k * TT;
+    const int nvalid = min(TT, eff_end - tile_start);
+    if (tile_start != cur_start) {
+      cur_blk_i = tile_start / p.block_size;
+      cur_in = tile_start - cur_blk_i * p.block_size;
+    }
+    if (cur_blk_i != cached_blk_i) {
+      int blk = cur_blk_i == pf_i ? pf_blk : table_entry(cur_blk_i);
+      if (blk < 0 || blk >= p.num_blocks) { blk = 0; bad = true; }
+      cached_off = (int64_t)blk * p.block_size * kRowBytes;
+      cached_blk_i = cur_blk_i;
+      pf_i = cur_blk_i + 1 < npages_tab ? cur_blk_i + 1 : -1;
+      if (pf_i >= 0) pf_blk = table_entry(pf_i);
+    }
+    t_rsrc = make_rsrc(p.kv + cached_off + (int64_t)cur_in * kRowBytes, nvalid * kRowBytes);
+    cur_start = tile_start + TT;
+    cur_in += TT;
+    while (cur_in >= p.block_size) { cur_in -= p.block_size; ++cur_blk_i; }
+  };
+  auto dma_ins = [&](int i) {
+    if (i < kVw) {
+      const int m = kVw * wave + i;
+      const int gm = 8 * (m & 1) | 2 * ((m >> 2) & 1) | ((m >> 1) & 1);
+      dma_lds16(t_rsrc, t_lbase + m * 1024, (u_v ^ (16 * gm)) + h_v, 1152 * m);
+    } else if (wave < 2) {
+      dma_lds16(t_rsrc, t_lbase + kVRegion + wave * 1024, r_v, 9216 * wave);
+    }
+  };
+  auto issue_tile = [&](int k, int b) {
+    tile_setup(k, b);
+#pragma unroll
+    for (int i = 0; i < kNDw; ++i) dma_ins(i);
+  };
+  // Wait until at most `n` tile issues after the one awaited are in flight
+  // (every issue, real or empty, is the same instructions).
+  auto wait_issues = [&](auto n_tag) {
+    constexpr int n = decltype(n_tag)::value;
+    if (NW == 2 || wave >= 2) wait_vmcnt<n * kNIo>();
+    else wait_vmcnt<n * kNDw>();
+  };
+
+  // ---- LDS reads ----
+  // K: lane (token j, half h) reads the 32 bytes 64c + 32h .. +31 of row j
+  // (logical chunks 4c + 2h, 4c + 2h + 1); the swizzle makes that chunk
+  // pair (4 (c & 3) ^ (2h ^ swz_w(j))) (+1), i.e. byte offset
+  // (k_b ^ 64 (c & 3)) + 256 (c >> 2) and that ^ 16.  The rope step reads the
+  // rope row.
+  const int k_b = j * 512 + 16 * ((2 * h) ^ swz_w(j));
+  const int k_r = kVRegion + j * 64 + 16 * ((2 * h) ^ ((j >> 2) & 3));
+  auto load_k = [&](const char* buf, int c) -> i32x8 {
+    int o0, o1;
+    if (c < 8) {
+      o0 = (k_b ^ (64 * (c & 3))) + 256 * (c >> 2);
+      o1 = o0 ^ 16;
+    } else {
+      o0 = k_r;
+      o1 = k_r ^ 16;
+    }
+    const u32x4 lo = lds_load<u32x4>(buf, o0);
+    const u32x4 hi = lds_load<u32x4>(buf, o1);
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // V^T for dim block d: k-slot 32h' + 8q + e (q = 0, 1) of lane group G
+  // (h' = G / 2) is token 16q + 8 (e / 4) + 4h' + e % 4, the token order of
+  // the P^T operand below; k-slots 32h' + 16 .. +31 are zero.  Group G reads
+  // dims 32d + 16 (G % 2) .. +15 of row e = (lane / 2) % 8, half lane % 2:
+  // chunk (2 (d & 7) | (G & 1)) ^ swz_w(tv) at byte (v_b ^ 32 (d & 7)) +
+  // 256 (d >> 3), and 16 tokens on at +8192.
+  int v_b;
+  {
+    const int G = lane >> 4, e = (lane >> 1) & 7, jb = lane & 1;
+    const int tv = 8 * (e >> 2) + 4 * (G >> 1) + (e & 3);
+    v_b = tv * 512 + 16 * ((G & 1) ^ swz_w(tv)) + 8 * jb;
+  }
+  auto load_v = [&](const char* buf, int d, i32x8& v) {
+    const int off = (v_b ^ (32 * (d & 7))) + 256 * (d >> 3);
+    const i32x2 a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(buf + off));
+    const i32x2 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(buf + off + 8192));
+    v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
+  };
+
+  // ---- the stream ----
+  // The accumulator holds sum 2^(x - (m0 - kBias)) V over the keys so far,
+  // m0 the row's reference: P is e4m3 of p = 2^(x - (m_run - kBias)) <= 2^8
+  // with an integer running reference m_run that moves (to the ceiling of
+  // the tile max) only past kLazy, and the P.V MFMA scales P by the E8M0
+  // factor 2^(m_run - m0).  So the accumulator is only ever written by MFMAs
+  // and needs no rescaling.  (The scaled MFMA takes 64 tokens: a 32-token
+  // tile fills k-slots 0-15 of each lane half and zeros the rest, at half
+  // the MFMA rate, so that three tiles of the ring stay in flight.)  m0 is
+  // the ceiling of the row's first maximum; a row whose maximum later climbs
+  // more than 64 units above it (far inside the E8M0 range, and keeping
+  // 2^e V P inside fp32) sends the workgroup through the piece again with m0
+  // the ceiling of the exact maximum (second pass).
+  //
+  // Software pipeline, one iteration per tile k (S(k) = its scores, computed
+  // by the previous iteration):
+  //   A  wait until tile k+1 has landed, then a barrier (every wave's share
+  //      of it is in, and every wave is done with tile k-1's slot); resolve
+  //      the page of tile k+NBUF-1;
+  //   B  the QK MFMAs of tile k+1, with the softmax of S(k) (VALU) between
+  //      them;
+  //   C  the P.V MFMAs of tile k, with the DMA instructions of tile k+NBUF-1
+  //      (into tile k-1's slot) between them.
+  // The matrix pipe runs the MFMAs of a phase while the wave issues the
+  // phase's other work.  Tiles past the piece's end are issued as empty
+  // loads, so every wait counts the same instructions.
+  wait_vmcnt<0>();  // q is in registers before the DMA stream starts
+  f32x16 acc[16];
+  float m_true = -INFINITY, m_run = -INFINITY, m0 = -INFINITY, l_run = 0.f, lh_run = 0.f;
+  float m0_fixed = -INFINITY;  // second pass: the reference from the first pass's exact max
+  constexpr int kPK = 3;       // K operands in flight ahead of their MFMA
+  constexpr int kPV = 4;       // V^T operands in flight ahead of their MFMA
+  // V^T and P^T operands keep their upper four registers at zero
+  i32x8 vq[kPV];
+#pragma unroll
+  for (int i = 0; i < kPV; ++i) vq[i] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  i32x8 pop = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+
+  // QK of one tile as 9 chained steps; between step c and c+1 the caller's
+  // work(c) (c = 0..8) is issued, and work(-1) before the first.
+  auto qk_tile = [&](const char* buf, f32x16& s, auto&& work) {
+    i32x8 kq[kPK];
+#pragma unroll
+    for (int i = 0; i < kPK; ++i) kq[i] = load_k(buf, i);
+    work(std::integral_constant<int, -1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](auto c_tag) {
+      constexpr int c = decltype(c_tag)::value;
+      const i32x8 cur = kq[c % kPK];
+      if constexpr (c + kPK < 9) kq[c % kPK] = load_k(buf, c + kPK);
+      qk_step_w32<c == 0, c == 8>(s, cur, qop[c]);
+      work(c_tag);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    step(std::integral_constant<int, 4>{});
+    step(std::integral_constant<int, 5>{});
+    step(std::integral_constant<int, 6>{});
+    step(std::integral_constant<int, 7>{});
+    step(std::integral_constant<int, 8>{});
+  };
+  auto no_work = [](auto) {};
+
+  bool ovf = false;
+  // One iteration of the pipeline for tile k: S(k) in s_cur, S(k+1) into s_next.
+  auto iteration = [&](int k, const f32x16& s_cur, f32x16& s_next) {
+    const bool has_next = k + 1 < ntiles;
+    // ---- A ----
+    wait_issues(std::integral_constant<int, NBUF - 3>{});  // tile k+1 in
+    if constexpr (NW > 1) __syncthreads();
+    tile_setup(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- B: softmax of S(k) between the QK steps of tile k+1 ----
+    // Register r of S holds token 8 (r / 4) + 4h + r % 4 of the tile (the
+    // row's other 16 are in lane l ^ 32).
+    const int tile_start = seg_start + k * TT;
+    const int vis = end_row - tile_start - 4 * h;  // register r is visible iff 8 (r / 4) + r % 4 < vis
+    float x[16];
+    float mloc = -INFINITY;
+    float e = 0.f, m_ref = 0.f, psum = 0.f, hsum = 0.f;
+    int w[4];
+    auto softmax_part = [&](auto c_tag) {
+      constexpr int c = decltype(c_tag)::value;
+      if constexpr (c == -1) {
+        if (tile_start + TT <= end_min) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = s_cur[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = (8 * (i >> 2) + (i & 3)) < vis ? s_cur[i] : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
+      } else if constexpr (c == 0) {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+        mloc = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])) * sl2;
+        m_true = fmaxf(m_true, mloc);
+        if (mloc > m_run + Lazy<true>::kLazy) m_run = ceilf(mloc);
+        if (m0 == -INFINITY) m0 = m_run;
+        const bool live = m_run != -INFINITY;
+        e = live ? m_run - m0 : 0.f;  // an integer >= 0
+        ovf |= e > 64.f;              // keeps 2^e V P (and l) far inside fp32
+        // p = 2^(s sl2 - m_ref); a row without a visible key yet has every
+        // score at -inf and takes m_ref 0 (p = 0)
+        m_ref = live ? m_run - Lazy<true>::kBias : 0.f;
+      } else if constexpr (c >= 1 && c <= 4) {
+#pragma unroll
+        for (int i = 4 * (c - 1); i < 4 * c; ++i) x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl2, -m_ref));
+      } else if constexpr (c == 6) {
+        // P^T in e4m3: k-slot 32h + 4m + i (byte 4m + i) is token 8m + 4h + i,
+        // register 4m + i
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w[q] = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q], x[4 * q + 1], 0, false);
+          w[q] = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2], x[4 * q + 3], w[q], true);
+        }
+      }
+    };
+    // The row sums (exact p, and p as rounded to e4m3) go between the P.V
+    // steps.
+    auto sums_part = [&](int d) {
+      if (d == 1) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = x[i] + x[i + 8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] += t[i + 4];
+        psum = (t[0] + t[2]) + (t[1] + t[3]);
+      } else if (d == 3) {
+        float t[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], true);
+          t[q] = (a[0] + a[1]) + (b[0] + b[1]);
+        }
+        hsum = (t[0] + t[1]) + (t[2] + t[3]);
+      } else if (d == 5) {
+        const float se = __builtin_amdgcn_exp2f(e);  // exact: e is a small integer
+        l_run += se * psum;
+        lh_run += se * hsum;
+      }
+    };
+    if (has_next) {
+      qk_tile(lds[(k + 1) % NBUF], s_next, softmax_part);
+    } else {
+      softmax_part(std::integral_constant<int, -1>{});
+      softmax_part(std::integral_constant<int, 0>{});
+      softmax_part(std::integral_constant<int, 1>{});
+      softmax_part(std::integral_constant<int, 2>{});
+      softmax_part(std::integral_constant<int, 3>{});
+      softmax_part(std::integral_constant<int, 4>{});
+      softmax_part(std::integral_constant<int, 6>{});
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pop[q] = w[q];
+    const int scale_b = 127 + (int)fminf(e, 64.f);  // E8M0 2^e per row
+    const int scale_a = opaque(127);                // E8M0 1 for V^T
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- C: O^T += 2^e V^T . P^T over 16 dim blocks, with the DMA of tile
+    // k+NBUF-1 between them ----
+    const char* buf = lds[k % NBUF];
+#pragma unroll
+    for (int i = 0; i < kPV; ++i) load_v(buf, i, vq[i]);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      const i32x8 cur = vq[d % kPV];
+      if (d + kPV < 16) load_v(buf, d + kPV, vq[d % kPV]);
+      pv_step_w32(acc[d], cur, pop, scale_a, scale_b);
+#pragma unroll
+      for (int i = 0; i < kNDw; ++i)
+        if (i * 16 / kNDw == d) dma_ins(i);
+      sums_part(d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[d] = f32x16{};
+    m_true = -INFINITY;
+    m_run = m0 = m0_fixed;
+    l_run = lh_run = 0.f;
+    ovf = false;
+    cur_start = -1;
+    cached_blk_i = -1;
+    pf_i = -1;
+    if (ntiles > 0) {
+#pragma unroll
+      for (int k = 0; k < NBUF - 1; ++k) issue_tile(k, k);
+      f32x16 s_a, s_b;
+      wait_issues(std::integral_constant<int, NBUF - 2>{});  // tile 0 in
+      if constexpr (NW > 1) __syncthreads();
+      qk_tile(lds[0], s_a, no_work);
+      // two iterations per trip, so S(k) and S(k+1) alternate between s_a
+      // and s_b without copies
+      for (int k = 0; k < ntiles; ++k) {
+        iteration(k, s_a, s_b);
+        s_a = s_b;
+      }
+      wait_vmcnt<0>();  // the empty issues past the end have landed
+    }
+    mfma_settle_w32();  // the accumulator is read (or cleared) after this
+    if (__syncthreads_or(ovf ? 1 : 0) == 0) break;
+    // some row outran the reference's range: again, from the exact maximum
+    m0_fixed = ceilf(m_true);
+  }
+
+  // ---- the piece's result ----
+  // Row totals over the two lanes of a row; the accumulator and l refer to
+  // m0 - kBias: rescale to the exact max, and by l / lh for the rounded P.
+  auto pair_sum = [](float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  };
+  float l_tot = pair_sum(l_run);
+  const float lh_tot = pair_sum(lh_run);
+  const float f0 = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m0 - Lazy<true>::kBias) - m_true);
+  const float fo = lh_tot > 0.f ? f0 * (l_tot / lh_tot) : f0;
+  l_tot *= f0;
+  bad = __syncthreads_or(bad ? 1 : 0) != 0;
+  if (!rok) return;
+  float mult, stat0;
+  char* dst;
+  float* stat0_p;
+  float* stat1_p = nullptr;
+  int kind;  // 0 bf16, 1 fp16, 2 fp32
+  if (pc.mode == kOutFinal) {
+    // normalised output and natural-log LSE; a sink joins as one more logit
+    // with a zero value
+    const bool has = m_true > -INFINITY;
+    float lse = has ? kLn2 * (m_true + __log2f(l_tot)) : -INFINITY;
+    mult = has ? ks / l_tot : 0.f;
+    if (p.sinks) {
+      const float nl = logaddexp_f(lse, p.sinks[hh]);
+      mult = has ? mult * expf(lse - nl) : 0.f;
+      lse = nl;
+    }
+    if (bad) { lse = __builtin_nanf(""); mult = __builtin_nanf(""); }
+    const int64_t orow = (int64_t)(t0 + ti) * H + hh;
+    kind = p.out_dtype;
+    dst = (char*)p.out + orow * kKvRank * (kind == 2 ? 4 : 2);
+    stat0 = lse;
+    stat0_p = p.lse + orow;
+  } else {
+    const int64_t slot = pc.mode == kOutSegment ? ((int64_t)(t0 + ti) * H + hh) * p.num_segments + pc.s
+                                                : pc.prow0 + wave * 32 + j;
+    mult = ks;
+    // segment partials in fp32; the balanced split's piece partials in fp32
+    // for fp32 outputs, else in bf16
+    if (pc.mode == kOutSegment || p.out_dtype == 2) {
+      kind = 2;
+      dst = (char*)(p.seg_out + slot * kKvRank);
+    } else {
+      kind = 0;
+      dst = (char*)(p.piece_out + slot * kKvRank);
+    }
+    stat0 = bad ? __builtin_nanf("") : m_true;
+    stat0_p = p.seg_max + slot;
+    stat1_p = p.seg_sum + slot;
+  }
+  mult *= fo;
+  // register r of dim block d holds dim 32 d + 8 (r / 4) + 4 h + r % 4; one
+  // store loop per output kind (the kind is chosen outside the loop)
+  auto store_all = [&](auto kind_tag) {
+    constexpr int K = decltype(kind_tag)::value;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int dim = 32 * d + 8 * q + 4 * h;
+        const f32x4 o = f32x4{acc[d][4 * q], acc[d][4 * q + 1], acc[d][4 * q + 2], acc[d][4 * q + 3]} * mult;
+        if constexpr (K == 2) {
+          *(f32x4*)(dst + 4 * dim) = o;
+        } else {
+          u32x2 v;
+          if constexpr (K == 0) {
+            v[0] = (unsigned)f32_to_bf16_rne(o[0]) | ((unsigned)f32_to_bf16_rne(o[1]) << 16);
+            v[1] = (unsigned)f32_to_bf16_rne(o[2]) | ((unsigned)f32_to_bf16_rne(o[3]) << 16);
+          } else {
+            v[0] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[0]) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[1]) << 16);
+            v[1] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[2]) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[3]) << 16);
+          }
+          *(u32x2*)(dst + 2 * dim) = v;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if (kind == 2) store_all(std::integral_constant<int, 2>{});
+  else if (kind == 0) store_all(std::integral_constant<int, 0>{});
+  else store_all(std::integral_constant<int, 1>{});
+  if (h == 0) {
+    *stat0_p = stat0;
+    if (stat1_p) *stat1_p = l_tot;
+  }
+}
+
+// Two 16-row groups per wave run as the wide fp8 body (contiguous tiles).
+template <bool FP8, int RG, bool CONTIG>
+constexpr bool kWide = FP8 && RG == 2 && CONTIG;
+
 // Segment kernel: one workgroup per (segment, request, row chunk); the key
 // partition is the segment formula of the merge page's module description
 // (span = cdiv(len, S * TILE) * TILE; segment s = [s * span, min((s+1) * span, len))).
@@ -1180,7 +1807,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
   pc.r = r; pc.t0 = t0; pc.qlen = qlen; pc.L = L; pc.row0 = row0;
   pc.seg_start = seg_start; pc.seg_end = min(seg_start + span, L);
   pc.mode = kOutSegment; pc.s = s; pc.prow0 = 0; pc.phase = 0;
-  run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, 1, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, idx_buf, pc);
+  if constexpr (kWide<FP8, RG, CONTIG>)
+    run_piece_w32<NW, NBUF, QB>(p, lds, lds_address(&lds[0][0]), pc);
+  else
+    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, 1, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, idx_buf, pc);
 }
 
 // Work units of request r for a workgroup shape of rows_wg rows and TT-token
@@ -1296,7 +1926,10 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
     pc.s = 0;
     pc.prow0 = ((int64_t)gw * 2 + (pos == s_g ? 0 : 1)) * kRowsWG;
     pc.phase = (int)((pos - s_g) % KS);
-    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, KS, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, idx_buf, pc);
+    if constexpr (kWide<FP8, RG, CONTIG>)
+      run_piece_w32<NW, NBUF, QB>(p, lds, lds_address(&lds[0][0]), pc);
+    else
+      run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, KS, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, idx_buf, pc);
     pos += b - a;
   }
 }
@@ -1405,13 +2038,27 @@ void merge_kernel(MergeLaunch p) {
     }
     return true;
   };
+  // dims 8 lane .. 8 lane + 7 of piece row pr: fp32 segment partials, or
+  // split pieces (bf16 for 16-bit outputs)
+  const bool bf16_pieces = SPLIT && OUT != 2;
+  auto load_piece = [&](int64_t pr, f32x4& lo, f32x4& hi) {
+    if (bf16_pieces) {
+      const u32x4 b = *(const u32x4*)(p.piece_out + pr * kKvRank + 8 * lane);
+      lo = f32x4{__uint_as_float(b[0] << 16), __uint_as_float(b[0] & 0xffff0000u),
+                 __uint_as_float(b[1] << 16), __uint_as_float(b[1] & 0xffff0000u)};
+      hi = f32x4{__uint_as_float(b[2] << 16), __uint_as_float(b[2] & 0xffff0000u),
+                 __uint_as_float(b[3] << 16), __uint_as_float(b[3] & 0xffff0000u)};
+    } else {
+      const float* src = p.seg_out + pr * kKvRank + 8 * lane;
+      lo = *(const f32x4*)(src);
+      hi = *(const f32x4*)(src + 4);
+    }
+  };
   auto load_block = [&](f32x4 (&v)[2 * kBlk], int j0, unsigned long long pmask, int cnt) {
 #pragma unroll
     for (int u = 0; u < kBlk; ++u) {
       if (j0 + u < cnt && ((pmask >> (j0 + u)) & 1ull)) {
-        const float* src = p.seg_out + prow(j0 + u) * kKvRank + 8 * lane;
-        v[2 * u] = *(const f32x4*)(src);
-        v[2 * u + 1] = *(const f32x4*)(src + 4);
+        load_piece(prow(j0 + u), v[2 * u], v[2 * u + 1]);
       } else {
         v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -1476,9 +2123,7 @@ void merge_kernel(MergeLaunch p) {
 #pragma unroll
         for (int u = 0; u < kBlk; ++u) {
           if (j0 + u < cnt && ((pmask >> (j0 + u)) & 1ull)) {
-            const float* src = p.seg_out + prow(s0 + j0 + u) * kKvRank + 8 * lane;
-            v[2 * u] = *(const f32x4*)(src);
-            v[2 * u + 1] = *(const f32x4*)(src + 4);
+            load_piece(prow(s0 + j0 + u), v[2 * u], v[2 * u + 1]);
           } else {
             v[2 * u] = v[2 * u + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
@@ -1658,6 +2303,11 @@ hipError_t launch_any(const SegmentLaunch& a, const SegmentShape& sh, int split_
 // QB: bf16 q quantised in the q load (fp8 cache).
 template <bool FP8, bool CONTIG, bool QB = false>
 hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, int split_wgs, hipStream_t stream) {
+  if constexpr (FP8 && CONTIG) {
+    if (sh.rows_per_wave == 2) {  // wide waves: 32 rows each
+      return launch_any<true, 2, 2, true, QB>(a, sh, split_wgs, stream);
+    }
+  }
   switch (sh.waves) {
     case 1: return launch_any<FP8, 1, 1, CONTIG, QB>(a, sh, split_wgs, stream);
     case 2: return launch_any<FP8, 2, 1, CONTIG, QB>(a, sh, split_wgs, stream);
@@ -1698,6 +2348,20 @@ SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
   sh.fp8 = fp8;
   sh.rows_per_wave = 1;
   const int groups = (max_qlen * num_heads + 15) / 16;
+  if (fp8 && groups == 4 && tile >= 32) {
+    // 49-64 rows per chunk: two wide waves of 32 rows over contiguous
+    // 32-token tiles, two workgroups per CU.  (Measured at 52 x 16K: faster
+    // than four 16-row waves at 64 heads; slower at 48 heads, where the
+    // second wide wave would carry 16 empty rows, and with four wide waves
+    // for 96-head verify blocks.)
+    sh.rows_per_wave = 2;
+    sh.waves = 2;
+    const int rows_wg = 32 * sh.waves;
+    sh.chunks = (max_qlen * num_heads + rows_wg - 1) / rows_wg;
+    sh.contig = true;
+    sh.ks = 1;
+    return sh;
+  }
   // groups of 16 rows -> waves per workgroup
   if (groups <= 1)      { sh.waves = 1; }
   else if (groups == 2) { sh.waves = 2; }

@@ -281,6 +281,8 @@ def test_split_workspace_covers_two_slots_per_workgroup():
     assert (g, rows) == (7, 32)
     need = m.workspace_bytes(p)
     part_rows = g * 2 * rows
+    # fp32 piece rows (16-bit outputs use half as bf16), fp32 max and sum per
+    # row, the request unit offsets
     assert need >= part_rows * 512 * 4 + 2 * part_rows * 4 + (5 + 1) * 4
     # the segment partition of the same batch needs [T, H, S, 512] instead
     p.schedule = m.MLA_SCHEDULE_SEGMENTS
