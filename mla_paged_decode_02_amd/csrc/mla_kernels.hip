@@ -1829,6 +1829,15 @@ __device__ __forceinline__ int request_units(const SegmentLaunch& p, int r, int 
   return cdiv(qlen * p.num_heads, rows_wg) * cdiv(L, tt);
 }
 
+// Logical index of physical workgroup b of G when workgroup b runs on XCD
+// b % 8: XCD x holds logical indices [x q + min(x, r), ...) for G = 8 q + r,
+// in dispatch order (a bijection of [0, G)).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_major(int b, int G) {
+  const int x = b % kXcds, i = b / kXcds, q = G / kXcds, r = G % kXcds;
+  return x * q + min(x, r) + i;
+}
+
 // Inclusive prefix sum over the 64 lanes.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -1862,7 +1871,10 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
   const int lane = threadIdx.x & 63;
   const int R = p.num_reqs;
   const int G = gridDim.x;
-  const int gw = blockIdx.x;
+  // XCD-aware order: the dispatcher deals workgroups to the 8 XCDs in turn,
+  // so logical ranges are numbered XCD by XCD.  Neighbouring ranges (the
+  // pieces of one request, which load the same q rows) then share an L2.
+  const int gw = xcd_major(blockIdx.x, G);
 
   // Total units W (every wave computes the same values).
   int W = 0;
