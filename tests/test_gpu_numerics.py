@@ -12,6 +12,9 @@
   call bit for bit.
 * Malformed query ranges: a request whose qo_indptr range is longer than
   max_qlen gets NaN rows from every route, and the other requests are exact.
+* Rising logits: keys whose logits climb steadily drive the lazy running
+  max through many moves and, in the 32-row fp8 body, past the range of one
+  reference into the second pass.
 
 Every call goes through the C ABI (ctypes binding).
 """
@@ -113,6 +116,62 @@ def test_fp8_rows_with_two_to_five_keys(H, schedule):
     out, lse = m.decode(**mi.call_args(w, d), sinks=d["sinks"], schedule=schedule, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert_close(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l)
+
+
+def _rising_logits(H, lens, dtype, rise_per_32, seed):
+    """A batch whose logits climb steadily along each request's keys: all
+    heads of a request's token share rope dims u, and key j's rope dims are
+    c_j u with c_j set so that its base-2 logit grows by `rise_per_32` every
+    32 keys (plus the latent part, q's latent dims scaled to 1/4).  One piece
+    over L keys then sees its running max climb by rise_per_32 * L / 32
+    units: the lazy reference moves many times, and past 64 units the wide
+    fp8 body must take its second pass from the exact maximum."""
+    w = mi.make_workload(name="rising", seq_lens=lens, num_heads=H, block_size=64, dtype=dtype,
+                         sinks=True, seed=seed)
+    scale = w.kv_scale if dtype != "bf16" else None
+    vals = orc.decode(w.kv_cache.reshape(-1, 576), dtype, scale).reshape(w.kv_cache.shape)
+    poison = np.isnan(vals).any(axis=-1)
+    vals = np.where(np.isnan(vals), 0.0, vals)
+    q = orc.decode(w.q, dtype, w.q_scale if dtype != "bf16" else None).copy()
+    q[..., :512] *= 0.25
+    rng = np.random.default_rng(seed)
+    base2 = w.softmax_scale / orc.LOGE2
+    flat = vals.reshape(-1, 576)
+    for r in range(w.num_reqs):
+        t = int(w.qo_indptr[r])
+        u = rng.standard_normal(64)
+        q[t, :, 512:] = u
+        for j in range(int(w.seq_lens[r])):
+            row = orc.cache_row_index(w.block_table[r], j, w.block_size)
+            flat[row, 512:] = (rise_per_32 * j / 32.0) / (base2 * float(u @ u)) * u
+    codes, kscale = mi._encode(torch.from_numpy(vals.reshape(-1, 576).astype(np.float32)), dtype)
+    codes = codes.reshape(-1, 576)
+    codes[poison.reshape(-1)] = mi.BF16_NAN_BITS if dtype == "bf16" else mi.FP8_E4M3_NAN_BYTE
+    qc, qs = mi._encode(torch.from_numpy(q.astype(np.float32)), dtype)
+    return mi.with_(w, kv_cache=codes.reshape(w.kv_cache.shape), kv_scale=kscale, q=qc, q_scale=qs)
+
+
+@pytest.mark.parametrize("dtype,H,schedule,S", [
+    ("fp8_e4m3", 64, "segments", 1),   # 32-row waves, one piece per request: second pass
+    ("fp8_e4m3", 64, "balanced", 0),
+    ("fp8_e4m3", 48, "segments", 1),   # 16-row waves: repeated lazy rescales
+    ("fp8_e4m3", 16, "balanced", 0),   # k-split waves
+    ("bf16", 16, "segments", 1),
+    ("bf16", 128, "segments", 2),
+])
+def test_rising_logits(dtype, H, schedule, S):
+    import mla_paged_decode_02_amd as m
+    _print_case(f"rising logits {dtype} H={H} {schedule} S={S}")
+    w = _rising_logits(H, [8192, 3000, 700], dtype, 0.6, seed=1100 + H)
+    ref_o, ref_l = orc.mla_decode(w)
+    d = mi.to_torch(w, "cuda")
+    kw = {"num_segments": S} if schedule == "segments" else {}
+    out, lse = m.decode(**mi.call_args(w, d), sinks=d["sinks"], schedule=schedule, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    assert_close(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l)
+    # the construction does what it says: the largest logit sits at the end
+    # of each request, 0.6 * len / 32 base-2 units above the first key's
+    assert np.all(np.isfinite(ref_l))
 
 
 def _fresh_codes(w, seed):
