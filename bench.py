@@ -218,7 +218,7 @@ def time_schedule(w, ds, calls, schedule, args, torch, m, stream):
         tile = w.tile_size or m.tile_size_for_block(w.block_size)
         qlen_r = [int(x) for x in (w.qo_indptr[1:] - w.qo_indptr[:-1])]
         valid = sum(ql * len(m.segment_bounds(int(L), S, tile)) for L, ql in zip(w.seq_lens, qlen_r))
-        alg = kv_bytes + q_bytes + valid * H * (512 + 2) * 4
+        alg = kv_bytes + q_bytes + valid * H * (512 * 2 + 8)  # bf16 partials for the bf16 output
         kernel = "segment_kernel"
         res["num_segments"] = S
         res["segments_valid_rows"] = valid * H
@@ -382,7 +382,9 @@ def main():
         if args.extra:
             names += [n for n in OPTIONAL if n != args.workload]
         for name in names:
-            scheds = ["balanced", "segments"] if name in CORE else ["balanced"]
+            # both schedules for the benchmark configurations and the index
+            # streams (where the planner's segments beat the balanced split)
+            scheds = ["balanced", "segments"] if name in CORE or name.startswith("sparse") else ["balanced"]
             _, ls = time_workload(name, args, torch, m, mi, scheds)
             for ln in ls:
                 print(f"[bench] {name} {ln['schedule']}: {ln['us_per_step']} us/step", file=sys.stderr,

@@ -231,8 +231,10 @@ int mla_combine_lse(const void* shard_out, int32_t in_dtype, const float* shard_
  * mla_merge_segments.
  *  - schedule MLA_SCHEDULE_SEGMENTS: the segment partition above with
  *    S = num_segments, or with the planner's S (mla_resolve_num_segments) when
- *    num_segments == 0, then the merge (the same results as
- *    mla_decode_segments + mla_merge_segments with that S).
+ *    num_segments == 0, then the merge (the results of
+ *    mla_decode_segments + mla_merge_segments with that S: bit for bit with
+ *    an fp32 output; with a 16-bit output the fused call keeps its partials
+ *    in bf16, a rounding of the size of the output's own).
  *  - schedule MLA_SCHEDULE_BALANCED (num_segments must be 0): a balanced
  *    split of the key axis.  The batch's work is
  *    one sequence of units (request, row chunk, tile of TT keys) that is cut
@@ -240,8 +242,8 @@ int mla_combine_lse(const void* shard_out, int32_t in_dtype, const float* shard_
  *    same number of cache rows whatever the lengths.  A (request, row chunk)
  *    inside one range is finished by the first launch; one cut by a range
  *    boundary is merged by the second from per-piece base-2 partials (the
- *    same merge rule as above).  The result equals the num_segments >= 1
- *    result up to floating-point rounding.
+ *    same merge rule as above; bf16 partials for a 16-bit output).  The
+ *    result equals the segment schedule's up to floating-point rounding.
  */
 int mla_decode(const mla_problem* p, const float* sinks, void* out, int32_t out_dtype, float* lse,
                void* workspace, size_t workspace_bytes, void* stream);

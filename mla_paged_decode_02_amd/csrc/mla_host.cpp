@@ -522,6 +522,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
       if (stages & 1) {
         mla::SegmentLaunch a = make_launch(p, tile, 1, so, sm, ss);
         a.piece_out = po;
+        a.piece_bf16 = oc != 2;
         a.out = out;
         a.out_dtype = oc;
         a.lse = lse;
@@ -535,6 +536,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
         memset(&m, 0, sizeof(m));
         m.seg_out = so;
         m.piece_out = po;
+        m.piece_bf16 = oc != 2;
         m.seg_max = sm;
         m.seg_sum = ss;
         m.seq_lens = p->seq_lens;
@@ -569,8 +571,12 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
   float* so = reinterpret_cast<float*>(ws + w.out_off);
   float* sm = reinterpret_cast<float*>(ws + w.max_off);
   float* ss = reinterpret_cast<float*>(ws + w.sum_off);
+  // the fused call's partials: bf16 for a 16-bit output, else fp32
+  const bool piece_bf16 = oc != 2;
   if (stages & 1) {
     mla::SegmentLaunch a = make_launch(p, tile, S, so, sm, ss);
+    a.piece_out = reinterpret_cast<uint16_t*>(so);
+    a.piece_bf16 = piece_bf16;
     const mla::SegmentShape sh =
         mla::segment_shape(p->kv_dtype == MLA_DTYPE_FP8_E4M3, p->num_heads, a.max_qlen, tile);
     hipError_t e = mla::launch_segments(a, sh, 0, hs);
@@ -580,6 +586,8 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
     mla::MergeLaunch m;
     memset(&m, 0, sizeof(m));
     m.seg_out = so;
+    m.piece_out = reinterpret_cast<const uint16_t*>(so);
+    m.piece_bf16 = piece_bf16;
     m.seg_max = sm;
     m.seg_sum = ss;
     m.part_lens = nullptr;

@@ -66,11 +66,12 @@ struct SegmentLaunch {
   int32_t num_tokens, num_heads, num_reqs, max_qlen;
   int32_t causal, tile, num_segments;
   float softmax_scale;
-  // partial outputs: segment partials (fp32 seg_out), or the split kernel's
-  // piece partials (fp32 at seg_out when out_dtype is fp32, else bf16 at
-  // piece_out, the same memory); seg_max / seg_sum for both
+  // partial outputs: fp32 at seg_out, or, with piece_bf16 (the fused call
+  // with a 16-bit output), bf16 at piece_out (the same memory); seg_max /
+  // seg_sum in fp32 either way
   float* seg_out;
   unsigned short* piece_out;
+  int32_t piece_bf16;
   float* seg_max;
   float* seg_sum;
   // split kernel: finished rows go straight to the output
@@ -82,8 +83,9 @@ struct SegmentLaunch {
 };
 
 struct MergeLaunch {
-  const float* seg_out;             // segment partials, and split pieces for fp32 outputs
-  const unsigned short* piece_out;  // split pieces for 16-bit outputs (bf16)
+  const float* seg_out;             // fp32 partials
+  const unsigned short* piece_out;  // bf16 partials (piece_bf16), the same memory
+  int32_t piece_bf16;
   const float* seg_max;
   const float* seg_sum;
   const int32_t* part_lens;  // [T] or NULL -> derive from seq_lens / qo_indptr

@@ -294,7 +294,7 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
 template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, int KS = 1, bool QB = false>
 __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
                                           char (*lds)[TileGeom<FP8, TT>::kTileBytes], unsigned lds_u32,
-                                          int* phys_rows, int* idx_buf, const Piece& pc) {
+                                          int* idx_buf, const Piece& pc) {
   using F = KvFmt<FP8>;
   static_assert(TT == 32 || (TT == 16 && !FP8), "tile shape");
   constexpr int kNB = TT / 16;                         // 16-token blocks per tile
@@ -583,33 +583,37 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       const int pg_first = tile_start / p.block_size;
       const int pg_last = (tile_start + max(nvalid, 1) - 1) / p.block_size;
       if (pg_first < idx_pg0 || pg_last >= idx_pg0 + kIdxCap) load_idx(pg_first);
-      // Thread j < TT resolves tile row j (rows past the valid count resolve
-      // to tile row 0).
-      __syncthreads();  // previous readers of phys_rows are done
-      if (threadIdx.x < TT) {
-        const int j = tile_start + ((int)threadIdx.x < nvalid ? (int)threadIdx.x : 0);
+      // Lane j < TT of every wave resolves tile row j to its cache row (rows
+      // past the valid count resolve to tile row 0); the DMA instructions take
+      // the rows they need across lanes (a lane read for a row the whole
+      // instruction, or half of it, shares; a lane shuffle for per-lane rows),
+      // so no LDS round trip and no barrier per tile.
+      int phys = 0;
+      bool pbad = false;
+      if (lane < TT) {
+        const int j = tile_start + (lane < nvalid ? lane : 0);
         // pages of a power-of-two size (1 for index streams) divide by a shift
         const int blk_i = (p.block_size & (p.block_size - 1)) == 0 ? j >> __builtin_ctz(p.block_size)
                                                                      : j / p.block_size;
         const int blk = idx_buf[blk_i - idx_pg0];
-        phys_rows[threadIdx.x] =
-            (blk < 0 || blk >= p.num_blocks) ? -1 : blk * p.block_size + (j - blk_i * p.block_size);
+        pbad = blk < 0 || blk >= p.num_blocks;
+        phys = pbad ? 0 : blk * p.block_size + (j - blk_i * p.block_size);
       }
-      __syncthreads();
-      auto row_ptr = [&](int row) -> const char* {
-        int pr = phys_rows[row];
-        if (pr < 0) { pr = 0; bad = true; }
-        return p.kv + (int64_t)pr * kRowBytes;
-      };
+      if (__ballot(pbad)) bad = true;
+      auto row_base = [&](int pr) -> const char* { return p.kv + (int64_t)pr * kRowBytes; };
 #pragma unroll
       for (int i = 0; i < kVPerWave; ++i) {
         const int vi = wave + NW * i;
         const char* src;
         if constexpr (!FP8) {
-          src = row_ptr(vi) + (unsigned)(lane16 ^ (16 * F::swz_v(vi)));
+          const int pr = __builtin_amdgcn_readlane(phys, vi);
+          src = row_base(pr) + (unsigned)(lane16 ^ (16 * F::swz_v(vi)));
         } else {
+          // rows 2vi (lanes 0-31) and 2vi+1 (lanes 32-63)
+          const int p0 = __builtin_amdgcn_readlane(phys, 2 * vi);
+          const int p1 = __builtin_amdgcn_readlane(phys, 2 * vi + 1);
           const int row = 2 * vi + v_half;
-          src = row_ptr(row) + 16 * (v_cpos ^ F::swz_v(row));
+          src = row_base(v_half ? p1 : p0) + 16 * (v_cpos ^ F::swz_v(row));
         }
         dma_lds16_gather(lbase + vi * 1024, src);
       }
@@ -618,7 +622,8 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         const int ri = wave + NW * i;
         if (ri < kNIR) {
           const int row = ri * kRowsPerRope + rope_row_in;
-          const char* src = row_ptr(row) + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
+          const int pr = __shfl(phys, row);
+          const char* src = row_base(pr) + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
           dma_lds16_gather(lbase + (kNIV + ri) * 1024, src);
         }
       }
@@ -960,14 +965,13 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         stat1 = 0.f;
         stat1_p = nullptr;
       } else {
-        // segment partials in fp32; the balanced split's piece partials in
-        // fp32 for fp32 outputs, else in bf16 (a rounding of the size the
-        // 16-bit output takes anyway)
+        // partials in fp32, or in bf16 when the fused call's output is
+        // 16-bit (a rounding of the size that output takes anyway)
         const int64_t slot = pc.mode == kOutSegment
                                  ? ((int64_t)(t0 + ti[q]) * H + hh[q]) * p.num_segments + pc.s
                                  : pc.prow0 + (rgw * RG + q) * 16 + n;
         mult = ks;
-        if (pc.mode == kOutSegment || p.out_dtype == 2) {
+        if (!p.piece_bf16) {
           kind = 2;
           dst = (char*)(p.seg_out + slot * kKvRank + 16 * db0 + 4 * g);
         } else {
@@ -1708,9 +1712,8 @@ __device__ __forceinline__ void run_piece_w32(const SegmentLaunch& p, char (*lds
     const int64_t slot = pc.mode == kOutSegment ? ((int64_t)(t0 + ti) * H + hh) * p.num_segments + pc.s
                                                 : pc.prow0 + wave * 32 + j;
     mult = ks;
-    // segment partials in fp32; the balanced split's piece partials in fp32
-    // for fp32 outputs, else in bf16
-    if (pc.mode == kOutSegment || p.out_dtype == 2) {
+    // partials in fp32, or in bf16 when the fused call's output is 16-bit
+    if (!p.piece_bf16) {
       kind = 2;
       dst = (char*)(p.seg_out + slot * kKvRank);
     } else {
@@ -1771,7 +1774,6 @@ template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, bool
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void segment_kernel(
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][TileGeom<FP8, TT>::kTileBytes];
-  __shared__ int phys_rows[CONTIG ? 1 : TT];
   __shared__ int idx_buf[CONTIG ? 1 : kIdxCap];
   constexpr int kRowsWG = 16 * RG * NW;
   const int s = blockIdx.x;
@@ -1810,7 +1812,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
   if constexpr (kWide<FP8, RG, CONTIG>)
     run_piece_w32<NW, NBUF, QB>(p, lds, lds_address(&lds[0][0]), pc);
   else
-    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, 1, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, idx_buf, pc);
+    run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, 1, QB>(p, lds, lds_address(&lds[0][0]), idx_buf, pc);
 }
 
 // Work units of request r for a workgroup shape of rows_wg rows and TT-token
@@ -1865,7 +1867,6 @@ template <bool FP8, int NW, int RG, int NBUF, bool CONTIG, int TT, int OCC, int 
 __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void split_kernel(
     SegmentLaunch p) {
   __shared__ __attribute__((aligned(1024))) char lds[KS * NBUF][TileGeom<FP8, TT>::kTileBytes];
-  __shared__ int phys_rows[CONTIG ? 1 : TT];
   __shared__ int idx_buf[CONTIG ? 1 : kIdxCap];
   constexpr int kRowsWG = 16 * RG * NW;
   const int lane = threadIdx.x & 63;
@@ -1941,7 +1942,7 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
     if constexpr (kWide<FP8, RG, CONTIG>)
       run_piece_w32<NW, NBUF, QB>(p, lds, lds_address(&lds[0][0]), pc);
     else
-      run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, KS, QB>(p, lds, lds_address(&lds[0][0]), phys_rows, idx_buf, pc);
+      run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, KS, QB>(p, lds, lds_address(&lds[0][0]), idx_buf, pc);
     pos += b - a;
   }
 }
@@ -2050,9 +2051,8 @@ void merge_kernel(MergeLaunch p) {
     }
     return true;
   };
-  // dims 8 lane .. 8 lane + 7 of piece row pr: fp32 segment partials, or
-  // split pieces (bf16 for 16-bit outputs)
-  const bool bf16_pieces = SPLIT && OUT != 2;
+  // dims 8 lane .. 8 lane + 7 of piece row pr (fp32, or bf16 partials)
+  const bool bf16_pieces = p.piece_bf16 != 0;
   auto load_piece = [&](int64_t pr, f32x4& lo, f32x4& hi) {
     if (bf16_pieces) {
       const u32x4 b = *(const u32x4*)(p.piece_out + pr * kKvRank + 8 * lane);
