@@ -157,6 +157,13 @@ SWEEP = [
     # four-wave chunks with waves that hold no rows (40 heads; qlen 2 leaves a
     # 16-row chunk): a row-less wave issues the whole tile's loads
     ("fp8_e4m3", 40, 64, [900, 130], [2, 1], True, True, 3),
+    # 49-64 rows per chunk run the 32-row fp8 waves: causal verify blocks whose
+    # wave holds rows of two tokens with different causal limits (16 heads x
+    # qlen 4, 28 heads x qlen 2), and 52 heads with 12 empty rows in the second
+    # wave over 32-key pages
+    ("fp8_e4m3", 16, 64, [700, 2500, 40], [4, 3, 4], True, True, 3),
+    ("fp8_e4m3", 28, 64, [1300, 61], [2, 2], True, True, 2),
+    ("fp8_e4m3", 52, 32, [900, 333], None, False, True, 3),
 ]
 
 
