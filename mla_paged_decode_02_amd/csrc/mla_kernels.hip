@@ -1950,6 +1950,15 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
 // ---------------------------------------------------------------------------
 // Merge kernel
 // ---------------------------------------------------------------------------
+// floor(num / den) for 0 <= num < 2^48 and 0 < den < 2^31, through one fp64
+// division instead of a 64-bit integer division (a long instruction
+// sequence that also costs registers): the correctly rounded quotient is
+// within 2^-36 of num / den, which is an integer (then returned exactly) or
+// at least 1 / den from one.
+__device__ __forceinline__ int floor_div_exact(int64_t num, int64_t den) {
+  return (int)__builtin_floor((double)num / (double)den);
+}
+
 // Request of token t: the largest r with qo_indptr[r] <= t, found 64 entries
 // at a time (one load per lane and a ballot per level: one level for fewer
 // than 64 requests, two below 4096).
@@ -2009,7 +2018,8 @@ void merge_kernel(MergeLaunch p) {
   }
   int nv = 0;
   const int64_t base = row * S;
-  int64_t row_i0 = 0, first_row = 0, stride = 0, gf = 0, W = 1, G = 1;
+  // split pieces: rows of the piece buffers (below 2 G rows_wg, so 32-bit)
+  int row_i0 = 0, first_row = 0, stride = 0, gf = 0, W = 1, G = 1;
   if (malformed) {
   } else if constexpr (SPLIT) {
     const int t0 = p.qo_indptr ? p.qo_indptr[req] : req;
@@ -2021,13 +2031,13 @@ void merge_kernel(MergeLaunch p) {
     const int chunks = cdiv(qlen * p.num_heads, p.rows_wg);
     const int nt = units > 0 ? units / chunks : 0;
     if (nt > 0 && W > 0) {
-      const int64_t P = (int64_t)p.unit_offsets[req] + (int64_t)c * nt;
+      const int P = p.unit_offsets[req] + c * nt;
       G = p.grid_wgs;
-      gf = ((P + 1) * G - 1) / W;
-      const int64_t gl = ((P + nt) * G - 1) / W;
+      gf = floor_div_exact(((int64_t)P + 1) * G - 1, W);
+      const int gl = floor_div_exact(((int64_t)P + nt) * G - 1, W);
       if (gf == gl) return;  // finished by the split kernel
-      nv = (int)(gl - gf + 1);
-      const int64_t start_f = (gf * W) / G;
+      nv = gl - gf + 1;
+      const int start_f = floor_div_exact((int64_t)gf * W, G);
       row_i0 = (gf * 2 + (start_f < P ? 1 : 0)) * p.rows_wg + local;
       first_row = (gf * 2) * p.rows_wg + local;
       stride = 2 * p.rows_wg;
@@ -2041,13 +2051,13 @@ void merge_kernel(MergeLaunch p) {
   }
   // Row index of piece i in the partial buffers, and whether it exists.
   auto prow = [&](int i) -> int64_t {
-    if constexpr (SPLIT) return i == 0 ? row_i0 : first_row + (int64_t)i * stride;
+    if constexpr (SPLIT) return (int64_t)(i == 0 ? row_i0 : first_row + i * stride);
     return base + i;
   };
   auto present = [&](int i) -> bool {
     if constexpr (SPLIT) {
       const int64_t g = gf + i;
-      return ((g + 1) * W) / G > (g * W) / G;
+      return floor_div_exact((g + 1) * W, G) > floor_div_exact(g * W, G);
     }
     return true;
   };
