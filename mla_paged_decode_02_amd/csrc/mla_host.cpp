@@ -231,17 +231,19 @@ SplitPlan plan_split(const mla_problem* p, int tile) {
 }
 
 struct SplitWs {
-  size_t out_off, max_off, sum_off, off_off, total;
+  size_t out_off, max_off, sum_off, off_off, rec_off, total;
 };
 
-SplitWs split_ws(const SplitPlan& sp, int num_reqs) {
+SplitWs split_ws(const SplitPlan& sp, int num_reqs, int num_tokens) {
   SplitWs w;
   const size_t rows = (size_t)sp.grid_wgs * 2 * sp.rows_wg;
   w.out_off = 0;
   w.max_off = align256(rows * MLA_KV_LORA_RANK * sizeof(float));  // fp32 (or bf16) piece partials
   w.sum_off = w.max_off + align256(rows * sizeof(float));
   w.off_off = w.sum_off + align256(rows * sizeof(float));
-  w.total = w.off_off + align256((size_t)(num_reqs + 1) * sizeof(int32_t));
+  w.rec_off = w.off_off + align256((size_t)(num_reqs + 1) * sizeof(int32_t));
+  // per-token records (16 B each) and their flag, used with query ranges
+  w.total = w.rec_off + align256(((size_t)num_tokens + 1) * 4 * sizeof(int32_t));
   return w;
 }
 
@@ -375,7 +377,7 @@ int mla_decode_workspace_bytes(const mla_problem* p, size_t* bytes) {
   if (p->schedule == MLA_SCHEDULE_BALANCED) {
     const SplitPlan sp = plan_split(p, resolved_tile(p));
     if (sp.grid_wgs > 0) {
-      *bytes = split_ws(sp, p->num_reqs).total;
+      *bytes = split_ws(sp, p->num_reqs, p->num_tokens).total;
       return MLA_OK;
     }
   }
@@ -509,7 +511,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
   if (p->schedule == MLA_SCHEDULE_BALANCED) {
     const SplitPlan sp = plan_split(p, tile);
     if (sp.grid_wgs > 0) {
-      const SplitWs w = split_ws(sp, p->num_reqs);
+      const SplitWs w = split_ws(sp, p->num_reqs, p->num_tokens);
       if (!workspace || workspace_bytes < w.total)
         return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                     workspace ? workspace_bytes : (size_t)0);
@@ -519,6 +521,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
       float* sm = reinterpret_cast<float*>(ws + w.max_off);
       float* ss = reinterpret_cast<float*>(ws + w.sum_off);
       int32_t* offs = reinterpret_cast<int32_t*>(ws + w.off_off);
+      int32_t* recs = p->qo_indptr ? reinterpret_cast<int32_t*>(ws + w.rec_off) : nullptr;
       if (stages & 1) {
         mla::SegmentLaunch a = make_launch(p, tile, 1, so, sm, ss);
         a.piece_out = po;
@@ -528,6 +531,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
         a.lse = lse;
         a.sinks = sinks;
         a.unit_offsets = offs;
+        a.tok_rec = recs;
         hipError_t e = mla::launch_segments(a, sp.sh, sp.grid_wgs, hs);
         if (e != hipSuccess) return hip_fail(e, "split kernel launch");
       }
@@ -552,6 +556,7 @@ int decode_stages(const mla_problem* p, const float* sinks, void* out, int32_t o
         m.out_dtype = oc;
         m.lse = lse;
         m.unit_offsets = offs;
+        m.tok_rec = recs;
         m.rows_wg = sp.rows_wg;
         m.tt = sp.tt;
         m.grid_wgs = sp.grid_wgs;

@@ -80,6 +80,7 @@ struct SegmentLaunch {
   float* lse;
   const float* sinks;     // nullable
   int32_t* unit_offsets;  // [num_reqs + 1]: unit offset of each request, then the total
+  int32_t* tok_rec;       // nullable: [T + 1][4] per-token records for the merge, then a flag
 };
 
 struct MergeLaunch {
@@ -100,6 +101,7 @@ struct MergeLaunch {
   // balanced split pieces (unit_offsets != NULL): rows per workgroup, tile
   // tokens and workgroup count of the split kernel that wrote them
   const int32_t* unit_offsets;
+  const int32_t* tok_rec;  // nullable: the split kernel's per-token records
   int32_t rows_wg, tt, grid_wgs;
 };
 

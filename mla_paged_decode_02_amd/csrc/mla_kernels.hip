@@ -1831,6 +1831,28 @@ __device__ __forceinline__ int request_units(const SegmentLaunch& p, int r, int 
   return cdiv(qlen * p.num_heads, rows_wg) * cdiv(L, tt);
 }
 
+// Per-token records for the merge, written by one wave of the split kernel
+// (lane = request): for each query token t of the request, {first token of
+// the request, its unit offset, units per row chunk (0: no keys), total units
+// W} at tok_rec[4 t].  With them a merge wave finds its pieces, or that its
+// row was finished, in one load instead of a search over the query ranges.
+// They are only complete when the ranges tile the tokens: every qlen in
+// [0, max_qlen] here, and qo_indptr[0] == 0, qo_indptr[R] == T checked by the
+// caller, which then sets the flag word tok_rec[4 T]; otherwise the merge
+// searches.  Returns whether this lane's request passed its check.
+__device__ __forceinline__ bool write_token_records(const SegmentLaunch& p, bool real, int t0, int ql, int units,
+                                                    int offset, int W, int rows_wg) {
+  const bool ok = !real || (ql >= 0 && ql <= p.max_qlen);
+  const int n = (real && ok) ? ql : 0;
+  const int chunks = n > 0 ? cdiv(n * p.num_heads, rows_wg) : 1;
+  const i32x4 rec = {t0, offset, units > 0 ? units / chunks : 0, W};
+  for (int j = 0; __ballot(j < n); ++j) {
+    const int t = t0 + j;
+    if (j < n && t >= 0 && t < p.num_tokens) *(i32x4*)(p.tok_rec + 4 * (int64_t)t) = rec;
+  }
+  return ok;
+}
+
 // Logical index of physical workgroup b of G when workgroup b runs on XCD
 // b % 8: XCD x holds logical indices [x q + min(x, r), ...) for G = 8 q + r,
 // in dispatch order (a bijection of [0, G)).
@@ -1891,16 +1913,20 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
   const int64_t e_g = ((int64_t)(gw + 1) * W) / G;
 
   // First request whose units reach past s_g, and its unit offset; workgroup 0
-  // records every offset (and W) for the merge.
+  // records every offset (and W) for the merge, and with query ranges one
+  // record per token (see write_token_records).
   int r = -1;
   int base = 0;
   int carry = 0;
+  const bool recorder = gw == 0 && threadIdx.x < 64;
+  bool ranges_ok = true;
   for (int i = 0; i < R; i += 64) {
     int t0, ql, L;
     const int u = (i + lane < R) ? request_units(p, i + lane, kRowsWG, TT, &t0, &ql, &L) : 0;
     const int incl = wave_incl_scan(u);
     const int excl = carry + incl - u;
-    if (gw == 0 && threadIdx.x < 64 && i + lane < R) p.unit_offsets[i + lane] = excl;
+    if (recorder && i + lane < R) p.unit_offsets[i + lane] = excl;
+    if (recorder && p.tok_rec) ranges_ok &= write_token_records(p, i + lane < R, t0, ql, u, excl, W, kRowsWG);
     if (r < 0) {
       const unsigned long long hit = __ballot(u > 0 && excl <= s_g && s_g < (int64_t)excl + u);
       if (hit) {
@@ -1911,7 +1937,13 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
     }
     carry = __builtin_amdgcn_readfirstlane(carry + __shfl(incl, 63));
   }
-  if (gw == 0 && threadIdx.x == 0) p.unit_offsets[R] = W;
+  if (recorder && p.tok_rec) {
+    // valid only if the ranges tile [0, T) (qo_indptr[0] == 0 and
+    // qo_indptr[R] == T on top of the per-request checks)
+    const bool ok = __ballot(!ranges_ok) == 0 && p.qo_indptr[0] == 0 && p.qo_indptr[R] == p.num_tokens;
+    if (lane == 0) p.tok_rec[4 * p.num_tokens] = ok ? 1 : 0;
+  }
+  if (recorder && lane == 0) p.unit_offsets[R] = W;
   r = __builtin_amdgcn_readfirstlane(r);
   base = __builtin_amdgcn_readfirstlane(base);
   if (s_g >= e_g || r < 0) return;
@@ -2007,14 +2039,25 @@ void merge_kernel(MergeLaunch p) {
   const int h = (int)(row - (int64_t)t * p.num_heads);
   const int S = p.num_segments;
 
+  // The split kernel's token record, when its flag says the records are
+  // complete: the row's request start, unit offset and units per chunk in one
+  // load.  Else the request is found by searching the query ranges.
+  i32x4 rec = {0, 0, 0, 0};
+  bool have_rec = false;
+  if constexpr (SPLIT) {
+    if (p.tok_rec) {
+      rec = *(const i32x4*)(p.tok_rec + 4 * (int64_t)t);
+      have_rec = p.tok_rec[4 * (int64_t)p.num_tokens] != 0;
+    }
+  }
   int req = t;
   bool malformed = false;
-  if ((SPLIT || !p.part_lens) && p.qo_indptr) {
+  if (!have_rec && (SPLIT || !p.part_lens) && p.qo_indptr) {
     req = request_of_token(p.qo_indptr, p.num_reqs, t);
     // A request whose query range is malformed gets NaN rows (the stream
-    // kernels computed nothing for it).
+    // kernels computed nothing for it); so does a token outside every range.
     const int64_t a = p.qo_indptr[req], b = p.qo_indptr[req + 1];
-    malformed = a < 0 || b < a || b - a > p.max_qlen || b > p.num_tokens;
+    malformed = a < 0 || b < a || b - a > p.max_qlen || b > p.num_tokens || t < a || t >= b;
   }
   int nv = 0;
   const int64_t base = row * S;
@@ -2022,16 +2065,25 @@ void merge_kernel(MergeLaunch p) {
   int row_i0 = 0, first_row = 0, stride = 0, gf = 0, W = 1, G = 1;
   if (malformed) {
   } else if constexpr (SPLIT) {
-    const int t0 = p.qo_indptr ? p.qo_indptr[req] : req;
-    const int qlen = p.qo_indptr ? p.qo_indptr[req + 1] - t0 : 1;
+    int t0, P0, nt;  // the request's first token, unit offset, units per row chunk
+    if (have_rec) {
+      t0 = rec[0];
+      P0 = rec[1];
+      nt = rec[2];
+      W = rec[3];
+    } else {
+      t0 = p.qo_indptr ? p.qo_indptr[req] : req;
+      const int qlen = p.qo_indptr ? p.qo_indptr[req + 1] - t0 : 1;
+      P0 = p.unit_offsets[req];
+      const int units = p.unit_offsets[req + 1] - P0;
+      W = p.unit_offsets[p.num_reqs];
+      const int chunks = cdiv(qlen * p.num_heads, p.rows_wg);
+      nt = units > 0 ? units / chunks : 0;
+    }
     const int rr = (t - t0) * p.num_heads + h;  // row within the request
     const int c = rr / p.rows_wg, local = rr - c * p.rows_wg;
-    const int units = p.unit_offsets[req + 1] - p.unit_offsets[req];
-    W = p.unit_offsets[p.num_reqs];
-    const int chunks = cdiv(qlen * p.num_heads, p.rows_wg);
-    const int nt = units > 0 ? units / chunks : 0;
     if (nt > 0 && W > 0) {
-      const int P = p.unit_offsets[req] + c * nt;
+      const int P = P0 + c * nt;
       G = p.grid_wgs;
       gf = floor_div_exact(((int64_t)P + 1) * G - 1, W);
       const int gl = floor_div_exact(((int64_t)P + nt) * G - 1, W);

@@ -12,6 +12,10 @@
   call bit for bit.
 * Malformed query ranges: a request whose qo_indptr range is longer than
   max_qlen gets NaN rows from every route, and the other requests are exact.
+* Query ranges and the merge's token records: a batch with empty query
+  ranges (qlen 0) still tiles the tokens, so the merge reads the split
+  kernel's per-token records; a token that no range covers gets NaN rows
+  (the merge falls back to searching the ranges and finds none).
 * Rising logits: keys whose logits climb steadily drive the lazy running
   max through many moves and, in the 32-row fp8 body, past the range of one
   reference into the second pass.
@@ -251,3 +255,38 @@ def test_malformed_query_range_gives_nan_rows(route):
     out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
     assert np.isnan(out[:3]).all() and np.isnan(lse[:3]).all()
     assert_close(w, out, lse, ref_o, ref_l, reqs=[1], tok=np.array([3]))
+
+
+@pytest.mark.parametrize("route", ["balanced", "segments"])
+def test_empty_query_ranges(route):
+    """Requests 1 and 4 have no query tokens (qo_indptr repeats a value); the
+    other requests' rows match the oracle on both routes."""
+    import mla_paged_decode_02_amd as m
+    _print_case(f"empty query ranges {route}")
+    w = mi.make_workload(name="qlen0", seq_lens=[900, 300, 2500, 64, 700, 1], qlens=[2, 0, 3, 1, 0, 2],
+                         num_heads=32, block_size=64, dtype="fp8_e4m3", causal=True, sinks=True, seed=911)
+    ref_o, ref_l = orc.mla_decode(w)
+    d = mi.to_torch(w, "cuda")
+    out, lse = m.decode(**mi.call_args(w, d), sinks=d["sinks"], schedule=route, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l)
+
+
+@pytest.mark.parametrize("route", ["balanced", "segments"])
+def test_token_outside_every_range_gives_nan_rows(route):
+    """qo_indptr ends at 3 for a batch of 4 query tokens: token 3 belongs to no
+    request and gets NaN rows; tokens 0-2 are exact (non-causal, so token 2,
+    now request 1's only token, sees the same keys as before)."""
+    import mla_paged_decode_02_amd as m
+    _print_case(f"uncovered token {route}")
+    w = mi.make_workload(name="gap", seq_lens=[500, 1300], qlens=[2, 2], num_heads=16, block_size=64,
+                         dtype="bf16", causal=False, seed=913)
+    ref_o, ref_l = orc.mla_decode(w)
+    d = mi.to_torch(w, "cuda")
+    args = mi.call_args(w, d)
+    args["qo_indptr"] = torch.tensor([0, 2, 3], dtype=torch.int32, device="cuda")
+    out, lse = m.decode(**args, schedule=route, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert np.isnan(out[3]).all() and np.isnan(lse[3]).all()
+    assert_close(w, out, lse, ref_o, ref_l, tok=np.arange(3))
