@@ -266,7 +266,7 @@ int mla_decode_stage(const mla_problem* p, const float* sinks, void* out, int32_
  * GPU it runs on until the process ends; nothing is allocated or freed.  The
  * caller still passes q, the cache and the outputs.  160 MiB holds the
  * balanced split's partials for any batch on a 256-CU MI355X (at most
- * 32768 rows x 2 pieces x 2056 B); a segment partition needs
+ * 32768 rows x 2 pieces x 2056 B, plus 16 B per query token); a segment partition needs
  * T * H * S * 2056 B.  A batch whose mla_decode_workspace_bytes exceeds the
  * scratch size fails with MLA_ERR_WORKSPACE before any launch.  All calls on one GPU share the one
  * array: calls that overlap on a GPU (concurrent streams, threads) race and
