@@ -855,12 +855,20 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   };
 
   // acc *= alpha, one accumulator group at a time: keeps the AGPR -> VGPR ->
-  // AGPR round trip to four registers.
+  // AGPR round trip to four registers.  One wave per SIMD (OCC 1) keeps the
+  // accumulators in AGPRs; there the empty asm redefines the group in its
+  // AGPRs inside this rarely taken branch, as without it the compiler copies
+  // every accumulator to VGPRs at the top of each tile, on the path that does
+  // not rescale as well (bf16 at 16 heads: 1.1 us of 157 per step; the fp8
+  // body, with half the tiles, measured no gain).  With two waves per SIMD
+  // they live in VGPRs, and pinning them to AGPRs would split the register
+  // budget and spill.
   auto rescale_acc = [&](Acc& acc, const float (&alpha)[RG]) {
 #pragma unroll
     for (int q = 0; q < RG; ++q)
 #pragma unroll
       for (int d = 0; d < 32; ++d) {
+        if constexpr (OCC == 1 && !FP8) asm volatile("" : "+a"(acc[q][d]));
         acc[q][d] *= alpha[q];
         __builtin_amdgcn_sched_barrier(0);
       }
