@@ -29,6 +29,7 @@
 
 #include <mutex>
 #include <type_traits>
+#include <utility>
 #include <vector>
 
 #include "mla_internal.h"
@@ -1233,6 +1234,48 @@ __device__ __forceinline__ void pv_step_w32(f32x16& acc, const i32x8& v, const i
 }
 __device__ __forceinline__ void mfma_settle_w32() { asm volatile("s_nop 15\n\ts_nop 7"); }
 
+// A wide wave's result for its row (lane l holds row l % 32): register r of
+// dim block d holds dim 32 d + 8 (r / 4) + 4 h + r % 4 (h = l / 32); stored
+// times mult at dst as fp32 (kind 2), bf16 (0) or fp16 (1), one store loop
+// per kind (the kind is chosen outside the loop).
+__device__ __forceinline__ void store_w32(const f32x16 (&acc)[16], int h, float mult, char* dst, int kind) {
+  auto store_all = [&](auto kind_tag) {
+    constexpr int K = decltype(kind_tag)::value;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int dim = 32 * d + 8 * q + 4 * h;
+        const f32x4 o = f32x4{acc[d][4 * q], acc[d][4 * q + 1], acc[d][4 * q + 2], acc[d][4 * q + 3]} * mult;
+        if constexpr (K == 2) {
+          *(f32x4*)(dst + 4 * dim) = o;
+        } else {
+          u32x2 v;
+          if constexpr (K == 0) {
+            v[0] = (unsigned)f32_to_bf16_rne(o[0]) | ((unsigned)f32_to_bf16_rne(o[1]) << 16);
+            v[1] = (unsigned)f32_to_bf16_rne(o[2]) | ((unsigned)f32_to_bf16_rne(o[3]) << 16);
+          } else {
+            v[0] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[0]) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[1]) << 16);
+            v[1] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[2]) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[3]) << 16);
+          }
+          *(u32x2*)(dst + 2 * dim) = v;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if (kind == 2) store_all(std::integral_constant<int, 2>{});
+  else if (kind == 0) store_all(std::integral_constant<int, 0>{});
+  else store_all(std::integral_constant<int, 1>{});
+}
+
+template <typename F, int... C>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, C...>) {
+  (f(std::integral_constant<int, C>{}), ...);
+}
+
 template <int NW, int NBUF, bool QB>
 __device__ __forceinline__ void run_piece_w32(const SegmentLaunch& p, char (*lds)[18432], unsigned lds_u32,
                                               const Piece& pc) {
@@ -1733,47 +1776,446 @@ __device__ __forceinline__ void run_piece_w32(const SegmentLaunch& p, char (*lds
     stat1_p = p.seg_sum + slot;
   }
   mult *= fo;
-  // register r of dim block d holds dim 32 d + 8 (r / 4) + 4 h + r % 4; one
-  // store loop per output kind (the kind is chosen outside the loop)
-  auto store_all = [&](auto kind_tag) {
-    constexpr int K = decltype(kind_tag)::value;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int dim = 32 * d + 8 * q + 4 * h;
-        const f32x4 o = f32x4{acc[d][4 * q], acc[d][4 * q + 1], acc[d][4 * q + 2], acc[d][4 * q + 3]} * mult;
-        if constexpr (K == 2) {
-          *(f32x4*)(dst + 4 * dim) = o;
-        } else {
-          u32x2 v;
-          if constexpr (K == 0) {
-            v[0] = (unsigned)f32_to_bf16_rne(o[0]) | ((unsigned)f32_to_bf16_rne(o[1]) << 16);
-            v[1] = (unsigned)f32_to_bf16_rne(o[2]) | ((unsigned)f32_to_bf16_rne(o[3]) << 16);
-          } else {
-            v[0] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[0]) |
-                   ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[1]) << 16);
-            v[1] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[2]) |
-                   ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)o[3]) << 16);
-          }
-          *(u32x2*)(dst + 2 * dim) = v;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  if (kind == 2) store_all(std::integral_constant<int, 2>{});
-  else if (kind == 0) store_all(std::integral_constant<int, 0>{});
-  else store_all(std::integral_constant<int, 1>{});
+  store_w32(acc, h, mult, dst, kind);
   if (h == 0) {
     *stat0_p = stat0;
     if (stat1_p) *stat1_p = l_tot;
   }
 }
 
-// Two 16-row groups per wave run as the wide fp8 body (contiguous tiles).
+// ---------------------------------------------------------------------------
+// Wide waves (bf16): 32 query rows per wave
+// ---------------------------------------------------------------------------
+// The bf16 counterpart of the wide fp8 body.  A wave owns 32 rows and works on
+// 32x32 blocks with v_mfma_f32_32x32x16_bf16 (A lane l = row l%32, k
+// 8(l/32)..+7; B lane l = column l%32, the same k; D as for the fp8 body):
+//   S^T[token, row] = K . Q^T     32 latent steps of 16 dims + 4 rope steps
+//   O^T[dim, row]  += V^T . P^T   16 blocks of 32 dims x 2 steps of 16 tokens
+// Q^T takes 144 registers per lane and the accumulator the 256 AGPRs.  Each
+// K or V byte a wave reads from LDS feeds 32 rows (the 16-row bf16 shapes
+// feed 16), and both products run on the full-rate 32x32x16 instruction.
+//
+// The tile (32 tokens, 36 KiB) keeps the regions of KvFmt<false> (V rows of
+// 1024 B, rope rows of 128 B at +32 KiB, rope chunks swizzled by swz_r) with
+// its own V swizzle: chunk c of row r sits at c ^ swz_b(r).  swz_b's low four
+// bits are a bijection of r's, so the 16 rows one K read serves per pass land
+// in 16 distinct bank groups; a 16-bit transpose read serves 4 rows x 4
+// chunks per 32-lane pass, and those rows (r & 3 distinct) land in distinct
+// chunk quads.
+//
+// Softmax: P^T = bf16 of p = 2^(x - m0) for a fixed reference m0 per row, the
+// ceiling of the row's first maximum.  bf16 keeps fp32's exponent range, so p
+// needs no running rescale while the row's maximum stays within kBound of m0
+// (p <= 2^kBound); a row that climbs further sends the workgroup through the
+// piece again with m0 the ceiling of the exact maximum (second pass), as in
+// the fp8 body.  The accumulator is only ever written by MFMAs.
+__device__ __forceinline__ int swz_b(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// One step of S^T = K . Q^T (16 dims, bf16), result in VGPRs; wait states as
+// for qk_step_w32.
+template <bool FIRST, bool LAST>
+__device__ __forceinline__ void qk_step_w32b(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  static_assert(!(FIRST && LAST), "a tile has 36 steps");
+  if constexpr (FIRST) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "v"(q));
+  } else if constexpr (LAST) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 7"
+                 : "+v"(s) : "v"(k), "v"(q));
+  } else {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
+  }
+}
+
+// One P.V step O^T += V^T . P^T (16 tokens, bf16) on an AGPR accumulator;
+// wait states as for pv_step_w32.
+__device__ __forceinline__ void pv_step_w32b(f32x16& acc, const bf16x8& v, const bf16x8& pt) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(pt));
+}
+
+template <int NW, int NBUF>
+__device__ __forceinline__ void run_piece_w32b(const SegmentLaunch& p, char (*lds)[36864], unsigned lds_u32,
+                                               const Piece& pc) {
+  constexpr int TT = 32;                  // tokens per DMA tile (ring slot)
+  constexpr int kRowBytes = 1152;
+  constexpr int kTileBytes = TT * kRowBytes;
+  constexpr int kVRegion = TT * 1024;
+  constexpr int kRowsWG = 32 * NW;
+  constexpr int kVw = TT / NW;            // V rows per wave per tile (one instruction each)
+  constexpr int kRw = 4 / NW;             // rope instructions (8 rows each) per wave per tile
+  constexpr int kNDw = kVw + kRw;         // DMA instructions per wave per tile
+  constexpr float kBound = 32.f;          // p <= 2^kBound before a second pass
+  static_assert(kTileBytes == 36864, "bf16 32-token tiles");
+  static_assert(NW == 2 || NW == 4, "the wide body runs two or four waves");
+  static_assert(NBUF >= 3, "a tile in the P.V phase, one in the QK phase, and one in flight");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 31;  // the lane's query row in the wave
+  const int h = lane >> 5;
+
+  const int r = pc.r, t0 = pc.t0, qlen = pc.qlen, L = pc.L;
+  const int H = p.num_heads;
+  const int M = qlen * H;
+  const int row0 = pc.row0;
+  int64_t bt_base;
+  int cap;
+  page_list(p, r, &bt_base, &cap);
+  bt_base = __builtin_amdgcn_readfirstlane((int)(bt_base & 0xffffffff)) |
+            ((int64_t)__builtin_amdgcn_readfirstlane((int)(bt_base >> 32)) << 32);
+  cap = __builtin_amdgcn_readfirstlane(cap);
+  bool bad = L > cap;
+  const int seg_start = pc.seg_start;
+  const int seg_end = pc.seg_end;
+  const int last_row = min(row0 + kRowsWG, M) - 1;
+  const int lim_wg = p.causal ? (L - qlen + last_row / H + 1) : L;
+  const int eff_end = min(min(seg_end, lim_wg), cap);
+  const int ntiles = eff_end > seg_start ? cdiv(eff_end - seg_start, TT) : 0;
+
+  // The lane's query row (lanes l and l + 32 hold the same row).
+  const int row = row0 + wave * 32 + j;
+  const bool rok = row < M;
+  const int ti = rok ? row / H : 0;
+  const int hh = rok ? row - ti * H : 0;
+  const int lim = rok ? (p.causal ? max(0, L - qlen + ti + 1) : L) : 0;
+  const int end_row = min(seg_end, lim);
+  int end_min;  // keys every valid row of the wave sees: tiles below need no mask
+  {
+    int v = rok ? end_row : 0x7fffffff;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = min(v, __shfl_xor(v, off));
+    end_min = min(__builtin_amdgcn_readfirstlane(v), eff_end);
+  }
+
+  const float qs = p.q_scale ? *p.q_scale : 1.0f;
+  const float ks = p.kv_scale ? *p.kv_scale : 1.0f;
+  const float sl2 = p.softmax_scale * kLog2e * qs * ks;
+
+  // ---- Q^T operand: lane (j, h) holds row j's dims 16c + 8h .. +7 (c >= 32: rope) ----
+  bf16x8 qop[36];
+  {
+    const int64_t tok = t0 + ti;
+    const int64_t qoff = tok * p.q_stride_token + (int64_t)hh * p.q_stride_head;
+    const int64_t poff = p.q_pe ? tok * p.q_pe_stride_token + (int64_t)hh * p.q_pe_stride_head : qoff + kKvRank;
+    const __bf16* qb = (const __bf16*)p.q + qoff;
+    const __bf16* qr = (const __bf16*)(p.q_pe ? p.q_pe : p.q) + poff;
+#pragma unroll
+    for (int c = 0; c < 36; ++c) {
+      const __bf16* src = c < 32 ? qb + 16 * c + 8 * h : qr + 16 * (c - 32) + 8 * h;
+      const u32x4 v = rok ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
+      qop[c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // ---- DMA of one tile into ring slot b ----
+  // Instruction i < kVw of wave w fills V row m = kVw w + i: lane l writes
+  // physical chunk l and loads logical chunk l ^ swz_b(m) (the scalar row
+  // offset 1152 m in soffset).  Instruction kVw + i fills rope rows 8n ..
+  // 8n + 7, n = kRw w + i: lane l writes chunk l % 8 of row 8n + l / 8 and
+  // loads logical chunk (l % 8) ^ swz_r(8n + l / 8) = (l % 8) ^ (l / 16) ^
+  // 4 (n % 2).  The buffer descriptor covers the tile's valid rows only (rows
+  // past them read as zeros, which the softmax masks; a tile past the piece's
+  // end fetches nothing).  tile_setup resolves the tile's page through a
+  // scalar cursor over the page table; dma_ins issues one instruction, so the
+  // stream spreads them over the P.V MFMAs.
+  const int u_v = 16 * lane;
+  const int r_v = (lane >> 3) * kRowBytes + kKvRank * 2 + 16 * ((lane & 7) ^ (lane >> 4));
+  int cur_start = -1, cur_blk_i = 0, cur_in = 0, cached_blk_i = -1;
+  int64_t cached_off = 0;
+  int pf_i = -1, pf_blk = 0;
+  const int npages_tab = cap / p.block_size;
+  auto table_entry = [&](int i) {
+    return ((const __attribute__((address_space(4))) int*)p.block_table)[bt_base + (int64_t)i * p.bt_stride_col];
+  };
+  i32x4 t_rsrc;
+  unsigned t_lbase = 0;
+  auto tile_setup = [&](int k, int b) {
+    t_lbase = lds_u32 + (unsigned)(b * kTileBytes);
+    if (k >= ntiles) {
+      t_rsrc = make_rsrc(p.kv, 0);  // past the piece: fetches nothing
+      return;
+    }
+    const int tile_start = seg_start + k * TT;
+    const int nvalid = min(TT, eff_end - tile_start);
+    if (tile_start != cur_start) {
+      cur_blk_i = tile_start / p.block_size;
+      cur_in = tile_start - cur_blk_i * p.block_size;
+    }
+    if (cur_blk_i != cached_blk_i) {
+      int blk = cur_blk_i == pf_i ? pf_blk : table_entry(cur_blk_i);
+      if (blk < 0 || blk >= p.num_blocks) { blk = 0; bad = true; }
+      cached_off = (int64_t)blk * p.block_size * kRowBytes;
+      cached_blk_i = cur_blk_i;
+      pf_i = cur_blk_i + 1 < npages_tab ? cur_blk_i + 1 : -1;
+      if (pf_i >= 0) pf_blk = table_entry(pf_i);
+    }
+    t_rsrc = make_rsrc(p.kv + cached_off + (int64_t)cur_in * kRowBytes, nvalid * kRowBytes);
+    cur_start = tile_start + TT;
+    cur_in += TT;
+    while (cur_in >= p.block_size) { cur_in -= p.block_size; ++cur_blk_i; }
+  };
+  auto dma_ins = [&](int i) {
+    if (i < kVw) {
+      const int m = kVw * wave + i;
+      dma_lds16(t_rsrc, t_lbase + m * 1024, u_v ^ (16 * swz_b(m)), kRowBytes * m);
+    } else {
+      const int n = kRw * wave + (i - kVw);
+      dma_lds16(t_rsrc, t_lbase + kVRegion + n * 1024, r_v ^ (64 * (n & 1)), 8 * kRowBytes * n);
+    }
+  };
+  auto issue_tile = [&](int k, int b) {
+    tile_setup(k, b);
+#pragma unroll
+    for (int i = 0; i < kNDw; ++i) dma_ins(i);
+  };
+  // Wait until at most `n` tile issues after the one awaited are in flight
+  // (every wave issues the same kNDw instructions per tile, real or empty).
+  auto wait_issues = [&](auto n_tag) {
+    constexpr int n = decltype(n_tag)::value;
+    wait_vmcnt<n * kNDw>();
+  };
+
+  // ---- LDS reads ----
+  // K: lane (token j, half h) reads the 16 bytes of dims 16c + 8h .. +7 of
+  // row j, logical chunk 2c + h: byte (k_b ^ 32 (c & 7)) + 256 (c >> 3) in
+  // the V region, k_r ^ 32 (c - 32) in the rope region.
+  const int k_b = j * 1024 + 16 * (h ^ swz_b(j));
+  const int k_r = kVRegion + j * 128 + 16 * (h ^ KvFmt<false>::swz_r(j));
+  auto load_k = [&](const char* buf, int c) -> bf16x8 {
+    const int off = c < 32 ? (k_b ^ (32 * (c & 7))) + 256 * (c >> 3) : k_r ^ (32 * (c - 32));
+    return lds_load<bf16x8>(buf, off);
+  };
+  // V^T for dim block d, step s: k-slots 0-3 of lane half h' are tokens
+  // 16s + 4h' + e and k-slots 4-7 tokens 16s + 8 + 4h' + e (e = 0..3): the
+  // token order of the P^T operand below.  Lane 4i + jj of 16-lane group G
+  // (h' = G / 2) reads row 16s + 4h' + i (then + 8), dims 32d + 16 (G % 2) +
+  // 4jj .. +3: logical chunk 4d + 2 (G % 2) + jj / 2, half jj % 2.  Row + 8
+  // flips bit 1 of swz_b, row + 16 leaves it.
+  int v_b;
+  {
+    const int G = lane >> 4, i = (lane >> 2) & 3, jj = lane & 3;
+    const int ra = 4 * (G >> 1) + i;
+    v_b = ra * 1024 + 8 * (jj & 1) + 16 * ((2 * (G & 1) + (jj >> 1)) ^ swz_b(ra));
+  }
+  auto load_v = [&](const char* buf, int d, int s) -> bf16x8 {
+    const int oa = (v_b ^ (64 * (d & 3))) + 256 * (d >> 2) + 16384 * s;
+    const int ob = ((v_b ^ 32) ^ (64 * (d & 3))) + 256 * (d >> 2) + 16384 * s + 8192;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(buf + oa));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(buf + ob));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // ---- the stream ----
+  // Software pipeline, one iteration per tile k (S(k) computed by the
+  // previous iteration), as in the fp8 body:
+  //   A  wait until tile k+1 has landed, then a barrier; resolve the page of
+  //      tile k+NBUF-1;
+  //   B  the QK MFMAs of tile k+1, with the softmax of S(k) between them;
+  //   C  the P.V MFMAs of tile k, with the DMA of tile k+NBUF-1 (into tile
+  //      k-1's slot) between them.
+  wait_vmcnt<0>();  // q is in registers before the DMA stream starts
+  f32x16 acc[16];
+  float m_true = -INFINITY, m0 = -INFINITY, l_run = 0.f;
+  float m0_fixed = -INFINITY;  // second pass: the reference from the first pass's exact max
+  constexpr int kPK = 3;       // K operands in flight ahead of their MFMA
+  constexpr int kPV = 4;       // V^T operands in flight ahead of their MFMA
+
+  // QK of one tile as 36 chained steps; between step c and c+1 the caller's
+  // work(c) is issued, and work(-1) before the first.
+  auto qk_tile = [&](const char* buf, f32x16& s, auto&& work) {
+    bf16x8 kq[kPK];
+#pragma unroll
+    for (int i = 0; i < kPK; ++i) kq[i] = load_k(buf, i);
+    work(std::integral_constant<int, -1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](auto c_tag) {
+      constexpr int c = decltype(c_tag)::value;
+      const bf16x8 cur = kq[c % kPK];
+      if constexpr (c + kPK < 36) kq[c % kPK] = load_k(buf, c + kPK);
+      qk_step_w32b<c == 0, c == 35>(s, cur, qop[c]);
+      work(c_tag);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    unroll_seq(step, std::make_integer_sequence<int, 36>{});
+  };
+  auto no_work = [](auto) {};
+
+  bool ovf = false;
+  auto iteration = [&](int k, const f32x16& s_cur, f32x16& s_next) {
+    const bool has_next = k + 1 < ntiles;
+    // ---- A ----
+    wait_issues(std::integral_constant<int, NBUF - 3>{});  // tile k+1 in
+    __syncthreads();
+    tile_setup(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- B: softmax of S(k) between the QK steps of tile k+1 ----
+    // Register r of S holds token 8 (r / 4) + 4h + r % 4 of the tile (the
+    // row's other 16 are in lane l ^ 32).
+    const int tile_start = seg_start + k * TT;
+    const int vis = end_row - tile_start - 4 * h;  // register r is visible iff 8 (r / 4) + r % 4 < vis
+    float x[16];
+    float mloc = -INFINITY, m_ref = 0.f;
+    bf16x8 pop[2];
+    auto softmax_part = [&](auto c_tag) {
+      constexpr int c = decltype(c_tag)::value;
+      if constexpr (c == -1) {
+        if (tile_start + TT <= end_min) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = s_cur[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = (8 * (i >> 2) + (i & 3)) < vis ? s_cur[i] : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
+      } else if constexpr (c == 0) {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+        mloc = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])) * sl2;
+        m_true = fmaxf(m_true, mloc);
+        if (m0 == -INFINITY && mloc > -INFINITY) m0 = ceilf(mloc);
+        ovf |= mloc > m0 + kBound;
+        // p = 2^(s sl2 - m_ref); a row without a visible key yet has every
+        // score at -inf and takes m_ref 0 (p = 0)
+        m_ref = m0 > -INFINITY ? m0 : 0.f;
+      } else if constexpr (c >= 1 && c <= 4) {
+#pragma unroll
+        for (int i = 4 * (c - 1); i < 4 * c; ++i) x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl2, -m_ref));
+      } else if constexpr (c == 6) {
+        // P^T of step s: k-slot e is register 8s + e (token 16s + 8 (e / 4) + 4h + e % 4)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pop[s][e] = (__bf16)x[8 * s + e];
+      } else if constexpr (c == 8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = x[i] + x[i + 8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] += t[i + 4];
+        l_run += (t[0] + t[2]) + (t[1] + t[3]);
+      }
+    };
+    if (has_next) {
+      qk_tile(lds[(k + 1) % NBUF], s_next, softmax_part);
+    } else {
+      softmax_part(std::integral_constant<int, -1>{});
+      softmax_part(std::integral_constant<int, 0>{});
+      softmax_part(std::integral_constant<int, 1>{});
+      softmax_part(std::integral_constant<int, 2>{});
+      softmax_part(std::integral_constant<int, 3>{});
+      softmax_part(std::integral_constant<int, 4>{});
+      softmax_part(std::integral_constant<int, 6>{});
+      softmax_part(std::integral_constant<int, 8>{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- C: O^T += V^T . P^T over 16 dim blocks x 2 token steps, with the
+    // DMA of tile k+NBUF-1 between them ----
+    const char* buf = lds[k % NBUF];
+    bf16x8 vq[kPV];
+#pragma unroll
+    for (int i = 0; i < kPV; ++i) vq[i] = load_v(buf, i >> 1, i & 1);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const bf16x8 cur = vq[t % kPV];
+      if (t + kPV < 32) vq[t % kPV] = load_v(buf, (t + kPV) >> 1, (t + kPV) & 1);
+      pv_step_w32b(acc[t >> 1], cur, pop[t & 1]);
+#pragma unroll
+      for (int i = 0; i < kNDw; ++i)
+        if (i * 32 / kNDw == t) dma_ins(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[d] = f32x16{};
+    m_true = -INFINITY;
+    m0 = m0_fixed;
+    l_run = 0.f;
+    ovf = false;
+    cur_start = -1;
+    cached_blk_i = -1;
+    pf_i = -1;
+    if (ntiles > 0) {
+#pragma unroll
+      for (int k = 0; k < NBUF - 1; ++k) issue_tile(k, k);
+      f32x16 s_a, s_b;
+      wait_issues(std::integral_constant<int, NBUF - 2>{});  // tile 0 in
+      __syncthreads();
+      qk_tile(lds[0], s_a, no_work);
+      for (int k = 0; k < ntiles; ++k) {
+        iteration(k, s_a, s_b);
+        s_a = s_b;
+      }
+      wait_vmcnt<0>();  // the empty issues past the end have landed
+    }
+    mfma_settle_w32();  // the accumulator is read (or cleared) after this
+    if (__syncthreads_or(ovf ? 1 : 0) == 0) break;
+    // some row outran the reference's range: again, from the exact maximum
+    m0_fixed = ceilf(m_true);
+  }
+
+  // ---- the piece's result ----
+  // Row totals over the two lanes of a row; the accumulator and l refer to
+  // m0: rescale to the exact max.
+  auto pair_sum = [](float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  };
+  float l_tot = pair_sum(l_run);
+  const float f0 = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m0 - m_true);
+  l_tot *= f0;
+  bad = __syncthreads_or(bad ? 1 : 0) != 0;
+  if (!rok) return;
+  float mult, stat0;
+  char* dst;
+  float* stat0_p;
+  float* stat1_p = nullptr;
+  int kind;  // 0 bf16, 1 fp16, 2 fp32
+  if (pc.mode == kOutFinal) {
+    // normalised output and natural-log LSE; a sink joins as one more logit
+    // with a zero value
+    const bool has = m_true > -INFINITY;
+    float lse = has ? kLn2 * (m_true + __log2f(l_tot)) : -INFINITY;
+    mult = has ? ks / l_tot : 0.f;
+    if (p.sinks) {
+      const float nl = logaddexp_f(lse, p.sinks[hh]);
+      mult = has ? mult * expf(lse - nl) : 0.f;
+      lse = nl;
+    }
+    if (bad) { lse = __builtin_nanf(""); mult = __builtin_nanf(""); }
+    const int64_t orow = (int64_t)(t0 + ti) * H + hh;
+    kind = p.out_dtype;
+    dst = (char*)p.out + orow * kKvRank * (kind == 2 ? 4 : 2);
+    stat0 = lse;
+    stat0_p = p.lse + orow;
+  } else {
+    const int64_t slot = pc.mode == kOutSegment ? ((int64_t)(t0 + ti) * H + hh) * p.num_segments + pc.s
+                                                : pc.prow0 + wave * 32 + j;
+    mult = ks;
+    if (!p.piece_bf16) {
+      kind = 2;
+      dst = (char*)(p.seg_out + slot * kKvRank);
+    } else {
+      kind = 0;
+      dst = (char*)(p.piece_out + slot * kKvRank);
+    }
+    stat0 = bad ? __builtin_nanf("") : m_true;
+    stat0_p = p.seg_max + slot;
+    stat1_p = p.seg_sum + slot;
+  }
+  mult *= f0;
+  store_w32(acc, h, mult, dst, kind);
+  if (h == 0) {
+    *stat0_p = stat0;
+    if (stat1_p) *stat1_p = l_tot;
+  }
+}
+
+// Two 16-row groups per wave run as a wide body (contiguous tiles).
 template <bool FP8, int RG, bool CONTIG>
-constexpr bool kWide = FP8 && RG == 2 && CONTIG;
+constexpr bool kWide = RG == 2 && CONTIG;
 
 // Segment kernel: one workgroup per (segment, request, row chunk); the key
 // partition is the segment formula of the merge page's module description
@@ -1817,8 +2259,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)
   pc.r = r; pc.t0 = t0; pc.qlen = qlen; pc.L = L; pc.row0 = row0;
   pc.seg_start = seg_start; pc.seg_end = min(seg_start + span, L);
   pc.mode = kOutSegment; pc.s = s; pc.prow0 = 0; pc.phase = 0;
-  if constexpr (kWide<FP8, RG, CONTIG>)
+  if constexpr (kWide<FP8, RG, CONTIG> && FP8)
     run_piece_w32<NW, NBUF, QB>(p, lds, lds_address(&lds[0][0]), pc);
+  else if constexpr (kWide<FP8, RG, CONTIG>)
+    run_piece_w32b<NW, NBUF>(p, lds, lds_address(&lds[0][0]), pc);
   else
     run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, 1, QB>(p, lds, lds_address(&lds[0][0]), idx_buf, pc);
 }
@@ -1979,8 +2423,10 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
     pc.s = 0;
     pc.prow0 = ((int64_t)gw * 2 + (pos == s_g ? 0 : 1)) * kRowsWG;
     pc.phase = (int)((pos - s_g) % KS);
-    if constexpr (kWide<FP8, RG, CONTIG>)
+    if constexpr (kWide<FP8, RG, CONTIG> && FP8)
       run_piece_w32<NW, NBUF, QB>(p, lds, lds_address(&lds[0][0]), pc);
+    else if constexpr (kWide<FP8, RG, CONTIG>)
+      run_piece_w32b<NW, NBUF>(p, lds, lds_address(&lds[0][0]), pc);
     else
       run_piece<FP8, NW, RG, NBUF, CONTIG, TT, OCC, KS, QB>(p, lds, lds_address(&lds[0][0]), idx_buf, pc);
     pos += b - a;
@@ -2390,6 +2836,9 @@ hipError_t launch_seg_shape(const SegmentLaunch& a, const SegmentShape& sh, int 
       return launch_any<true, 2, 2, true, QB>(a, sh, split_wgs, stream);
     }
   }
+  if constexpr (!FP8 && CONTIG) {
+    if (sh.rows_per_wave == 2) return launch_any<false, 4, 2, true>(a, sh, split_wgs, stream);
+  }
   switch (sh.waves) {
     case 1: return launch_any<FP8, 1, 1, CONTIG, QB>(a, sh, split_wgs, stream);
     case 2: return launch_any<FP8, 2, 1, CONTIG, QB>(a, sh, split_wgs, stream);
@@ -2438,6 +2887,17 @@ SegmentShape segment_shape(bool fp8, int num_heads, int max_qlen, int tile) {
     // for 96-head verify blocks.)
     sh.rows_per_wave = 2;
     sh.waves = 2;
+    const int rows_wg = 32 * sh.waves;
+    sh.chunks = (max_qlen * num_heads + rows_wg - 1) / rows_wg;
+    sh.contig = true;
+    sh.ks = 1;
+    return sh;
+  }
+  if (!fp8 && groups >= 5 && tile >= 32) {
+    // more than 64 rows per chunk: four wide bf16 waves of 32 rows over
+    // contiguous 32-token tiles, one workgroup per CU
+    sh.rows_per_wave = 2;
+    sh.waves = 4;
     const int rows_wg = 32 * sh.waves;
     sh.chunks = (max_qlen * num_heads + rows_wg - 1) / rows_wg;
     sh.contig = true;

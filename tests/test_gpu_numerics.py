@@ -128,8 +128,9 @@ def _rising_logits(H, lens, dtype, rise_per_32, seed):
     c_j u with c_j set so that its base-2 logit grows by `rise_per_32` every
     32 keys (plus the latent part, q's latent dims scaled to 1/4).  One piece
     over L keys then sees its running max climb by rise_per_32 * L / 32
-    units: the lazy reference moves many times, and past 64 units the wide
-    fp8 body must take its second pass from the exact maximum."""
+    units: the lazy reference moves many times, and past 64 units (32 in
+    bf16) the wide bodies must take their second pass from the exact
+    maximum."""
     w = mi.make_workload(name="rising", seq_lens=lens, num_heads=H, block_size=64, dtype=dtype,
                          sinks=True, seed=seed)
     scale = w.kv_scale if dtype != "bf16" else None
@@ -161,7 +162,8 @@ def _rising_logits(H, lens, dtype, rise_per_32, seed):
     ("fp8_e4m3", 48, "segments", 1),   # 16-row waves: repeated lazy rescales
     ("fp8_e4m3", 16, "balanced", 0),   # k-split waves
     ("bf16", 16, "segments", 1),
-    ("bf16", 128, "segments", 2),
+    ("bf16", 128, "segments", 2),      # 32-row bf16 waves: second pass past 32 units
+    ("bf16", 128, "balanced", 0),
 ])
 def test_rising_logits(dtype, H, schedule, S):
     import mla_paged_decode_02_amd as m

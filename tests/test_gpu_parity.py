@@ -200,6 +200,8 @@ def test_planner_choice_and_empty_requests(schedule):
     ("fp8_e4m3", 64, 48, False),   # 32-row waves against 16-row waves
     ("bf16", 64, 48, True),
     ("bf16", 48, 16, False),
+    ("bf16", 128, 80, True),       # both four 32-row waves
+    ("bf16", 128, 64, False),      # 32-row waves against 16-row waves
 ])
 def test_head_count_independent(dtype, H, Hs, same_shape):
     """Heads are independent (no head folding): the first Hs heads of an
