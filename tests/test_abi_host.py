@@ -217,9 +217,12 @@ def test_split_plan_shapes():
     g, rows, tt = m.split_plan(_split_problem(H=16))
     assert (rows, tt) == (16, 16) and 1 <= g <= 1024
     assert m.split_plan(_split_problem(H=16, dtype=torch.float8_e4m3fn))[1:] == (16, 32)
-    # 64 heads: four waves of 16 rows; 128 heads: eight
+    # fp8, 64 heads: two wide waves of 32 rows over 32-token tiles
     assert m.split_plan(_split_problem(H=64, dtype=torch.float8_e4m3fn))[1:] == (64, 32)
-    assert m.split_plan(_split_problem(H=128, block=256))[1:] == (128, 16)
+    # bf16, 128 heads: four wide waves of 32 rows over 32-token tiles; pages
+    # shorter than a tile gather rows for eight 16-row waves over 16-token tiles
+    assert m.split_plan(_split_problem(H=128, block=256))[1:] == (128, 32)
+    assert m.split_plan(_split_problem(H=128, block=16))[1:] == (128, 16)
     # never more workgroups than units: 4 requests x cdiv(1000, 16) tiles
     assert m.split_plan(_split_problem(H=16))[0] <= 4 * (63 + 1)
 
