@@ -236,14 +236,34 @@ def test_split_plan_aligns_uniform_batches():
     assert m.split_plan(_split_problem(H=16, R=100, L=200))[0] == 200     # 2 per request
     assert m.split_plan(_split_problem(H=16, R=130, L=200))[0] == 256     # 130 < 192: all slots
     fp8 = torch.float8_e4m3fn
-    assert m.split_plan(_split_problem(H=64, R=52, L=1000, dtype=fp8))[0] == 468  # 9 x 52 of 512
+    # pages of 16 rows gather 32-token tiles: 1000 keys hold 32 tiles, and the
+    # 12-tile minimum per piece stops at half of the 512 slots: 4 x 52
+    assert m.split_plan(_split_problem(H=64, R=52, L=1000, dtype=fp8))[0] == 208
+    assert m.split_plan(_split_problem(H=64, R=52, L=1000, dtype=fp8, block=64))[0] == 468  # 9 x 52 of 512
     assert m.split_plan(_split_problem(H=128, R=52, L=200, block=256))[0] == 256  # 208 < 224
-    # gathered tiles (pages smaller than a tile) accept 3/4 at any shape
-    assert m.split_plan(_split_problem(H=128, R=52, L=200, block=1))[0] == 208
+    # gathered tiles (pages smaller than a tile) accept 3/4 at any shape; 200
+    # keys are 13 tiles, and the 12-tile minimum stops at half the slots
+    # (128): 2 x 52
+    assert m.split_plan(_split_problem(H=128, R=52, L=200, block=1))[0] == 104
     # unequal lengths (the summed lengths say so): every slot
     p = _split_problem(H=16, R=52, L=200)
     p.sum_seq_lens = 52 * 200 - 1
     assert m.split_plan(p)[0] == 256
+
+
+def test_gathered_pieces_keep_twelve_tiles():
+    """Index streams (page size 1) of 2048 keys at 16 heads: 128 tiles per
+    request, so at most 10 pieces per request under both schedules (the slots
+    alone would give 19); at 128 heads in fp8 (64 tiles of 32) the slots give
+    4 pieces, within the minimum."""
+    p = _split_problem(H=16, R=52, L=2048, block=1)
+    assert m.split_plan(p)[0] == 520
+    assert m.plan_num_segments(52, 2048, 16, tile_size=1, sum_seq_lens=52 * 2048) == 10
+    fp8 = torch.float8_e4m3fn
+    assert m.split_plan(_split_problem(H=128, R=52, L=2048, block=1, dtype=fp8))[0] == 208
+    assert m.plan_num_segments(52, 2048, 128, tile_size=1, sum_seq_lens=52 * 2048, kv_dtype="fp8_e4m3") == 4
+    # contiguous pages keep the slot formula
+    assert m.plan_num_segments(52, 2048, 16, tile_size=64, sum_seq_lens=52 * 2048) == 19
 
 
 def test_split_plan_respects_max_workgroups_and_segment_mode():
