@@ -2351,11 +2351,18 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
   // pieces of one request, which load the same q rows) then share an L2.
   const int gw = xcd_major(blockIdx.x, G);
 
+  // The first 64 requests' units, first tokens, query counts and lengths,
+  // one request per lane, loaded once: with at most 64 requests the two scans
+  // below and the piece loop read them from registers instead of reloading
+  // them one dependent round trip after another.
+  int u_l = 0, t0_l = 0, ql_l = 0, L_l = 0;
+  if (lane < R) u_l = request_units(p, lane, kRowsWG, TT, &t0_l, &ql_l, &L_l);
+
   // Total units W (every wave computes the same values).
   int W = 0;
   for (int i = 0; i < R; i += 64) {
     int t0, ql, L;
-    const int u = (i + lane < R) ? request_units(p, i + lane, kRowsWG, TT, &t0, &ql, &L) : 0;
+    const int u = i == 0 ? u_l : ((i + lane < R) ? request_units(p, i + lane, kRowsWG, TT, &t0, &ql, &L) : 0);
     W += __shfl(wave_incl_scan(u), 63);
   }
   // Lane shuffles read as divergent to the compiler: make the uniform values
@@ -2373,8 +2380,8 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
   const bool recorder = gw == 0 && threadIdx.x < 64;
   bool ranges_ok = true;
   for (int i = 0; i < R; i += 64) {
-    int t0, ql, L;
-    const int u = (i + lane < R) ? request_units(p, i + lane, kRowsWG, TT, &t0, &ql, &L) : 0;
+    int t0 = t0_l, ql = ql_l, L = L_l;
+    const int u = i == 0 ? u_l : ((i + lane < R) ? request_units(p, i + lane, kRowsWG, TT, &t0, &ql, &L) : 0);
     const int incl = wave_incl_scan(u);
     const int excl = carry + incl - u;
     if (recorder && i + lane < R) p.unit_offsets[i + lane] = excl;
@@ -2400,10 +2407,25 @@ __global__ __launch_bounds__(64 * NW * KS) __attribute__((amdgpu_waves_per_eu(OC
   base = __builtin_amdgcn_readfirstlane(base);
   if (s_g >= e_g || r < 0) return;
 
+  // The first request's fields come from the registers above (read once, as
+  // scalars, so they are not held through the tile loop); a workgroup that
+  // moves on to further requests loads theirs.
+  int t0, qlen, L, units;
+  if (r < 64) {
+    units = __builtin_amdgcn_readlane(u_l, r);
+    t0 = __builtin_amdgcn_readlane(t0_l, r);
+    qlen = __builtin_amdgcn_readlane(ql_l, r);
+    L = __builtin_amdgcn_readlane(L_l, r);
+  } else {
+    units = request_units(p, r, kRowsWG, TT, &t0, &qlen, &L);
+  }
   int64_t pos = s_g;
+  int loaded = r;  // the request whose fields t0, qlen, L, units hold
   while (pos < e_g && r < R) {
-    int t0, qlen, L;
-    const int units = request_units(p, r, kRowsWG, TT, &t0, &qlen, &L);
+    if (r != loaded) {
+      units = request_units(p, r, kRowsWG, TT, &t0, &qlen, &L);
+      loaded = r;
+    }
     if (pos >= base + units) {  // past this request (or it has no units)
       base += units;
       ++r;
