@@ -297,6 +297,28 @@ def test_split_parity_sweep(case, wgs):
                  ref_o, ref_l)
 
 
+@pytest.mark.parametrize("R,wgs", [(64, 0), (65, 0), (70, 7), (70, 37), (130, 0), (130, 11)])
+def test_split_many_requests(R, wgs):
+    """Batches of more than 64 requests: the split kernel keeps the first 64
+    requests' fields in registers and loads later ones, so workgroup ranges
+    that start past request 63, or that run from one side of it to the
+    other, must still find their pieces (ragged lengths, mixed query counts,
+    causal, sinks)."""
+    import mla_paged_decode_02_amd as m
+    _print_case(f"split many requests R={R} wgs={wgs}")
+    rng = np.random.default_rng(4000 + R)
+    lens = [int(x) for x in rng.integers(1, 400, R)]
+    qlens = [int(x) for x in rng.integers(1, 3, R)]
+    w = mi.make_workload(name="manyreq", seq_lens=lens, qlens=qlens, num_heads=16, block_size=16, dtype="bf16",
+                         causal=True, sinks=True, seed=4100 + R)
+    ref_o, ref_l = orc.mla_decode(w)
+    d = mi.to_torch(w, "cuda")
+    out, lse = m.decode(**mi.call_args(w, d), sinks=d["sinks"], schedule="balanced", max_workgroups=wgs,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
 def test_split_long_row_among_short_ones(dtype):
     """One long request among many short ones: the merge's step size follows
