@@ -368,6 +368,15 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   // that compute issue none.  (Eight waves would need more than vmcnt's 63
   // outstanding loads in one wave; the bf16 variant spills.)
   constexpr bool kProd = FP8 && CONTIG && KS == 1 && NW == 4;
+  // fp8 rows are 576 bytes, so every odd row starts half a 128-byte line in,
+  // and loading each row's latent and rope apart makes the tile's 18 DMA
+  // instructions touch 176 lines for its 144 (a plain DMA stream measured
+  // 5.9 TB/s that way, 6.8 TB/s over whole lines).  A lone wave (NW 1) loads
+  // whole lines instead and restores the layout with one exchange of 64
+  // chunks per tile (line_fix), before it reads the tile.  (A producer wave
+  // doing the same before the tile's barrier measured 3% slower at 48 heads:
+  // the exchange delays the three computing waves.)
+  constexpr bool kLineDma = FP8 && CONTIG && NW == 1;
   const int active_waves = cdiv(min(M - row0, kRowsWG), 16 * RG);
   const bool prod_mode = kProd && active_waves < NW;
   const bool is_producer = prod_mode && wave == NW - 1;
@@ -477,6 +486,19 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   const int v_cpos = lane % F::kVChunks;
   const int rope_row_in = lane / F::kRopeChunks;
   const int rope_cpos = lane % F::kRopeChunks;
+  // Whole-line fp8 tiles (kLineDma): the lane parts of the DMA offsets.  V
+  // instructions: (16 c) ^ (32 half) swizzled, plus 576 for the odd row; the
+  // row's rope chunk for the four displaced lanes.  Ninth-line instructions:
+  // lane 8i + e takes byte 16e of pair i's ninth line, as row 2i+1's latent
+  // chunk 28 + e (e < 4) or its rope chunk (e - 4) ^ swz_r (swz_r(2a+1) =
+  // ((lane >> 4) & 3) for a = 8ri + lane / 8).
+  const int lkey = (16 * v_cpos) ^ (32 * v_half);
+  const int h576 = v_half ? kRowBytes : 0;
+  const int rkey512 = kKvRank + 16 * (lane & 3);
+  const int lane4 = lane >> 2;
+  const int l8off = 2 * kRowBytes * (lane >> 3) +
+                    ((lane & 7) < 4 ? kRowBytes + 16 * (28 + (lane & 7))
+                                    : kRowBytes + kKvRank + 16 * (((lane & 7) - 4) ^ ((lane >> 4) & 3)));
 
   // Gathered tiles: a window of the request's page-table entries in LDS,
   // starting at page idx_pg0.  Every wave calls load_idx at the same tile;
@@ -526,12 +548,14 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         cached_blk_i = cur_blk_i;
       }
       // Buffer descriptor over the tile's rows (a guard: no offset below
-      // leaves them); per instruction a scalar row offset plus one 32-bit
-      // per-lane chunk offset.
-      const i32x4 rsrc = make_rsrc(p.kv + cached_off + (int64_t)cur_in * kRowBytes, TT * kRowBytes);
+      // leaves them; whole-line fp8 tiles cover only the valid rows, and
+      // what lies past them loads as zeros, finite data the softmax masks);
+      // per instruction a scalar row offset plus one 32-bit per-lane chunk
+      // offset.
+      const i32x4 rsrc = make_rsrc(p.kv + cached_off + (int64_t)cur_in * kRowBytes, (kLineDma ? nvalid : TT) * kRowBytes);
       const int key16 = opaque(lane16);
-      // Rows at or past the valid count load tile row 0; a full tile needs
-      // no clamp.
+      // Otherwise rows at or past the valid count load tile row 0; a full
+      // tile needs no clamp.
       auto dma_all = [&](auto full_tag) {
         constexpr bool kFull = decltype(full_tag)::value;
         auto clamp = [&](int row) { return kFull ? row : (row < nvalid ? row : 0); };
@@ -543,6 +567,20 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
           if constexpr (!FP8) {
             soff = clamp(vi) * kRowBytes;
             voff = key16 ^ (16 * F::swz_v(vi));
+          } else if constexpr (kLineDma) {
+            // rows 2vi and 2vi+1 are the tile's bytes 1152 vi .. +1151, nine
+            // 128-byte lines; this instruction reads the first eight whole:
+            // row 2vi's latent and rope, and row 2vi+1's latent chunks 0-27.
+            // The four lanes whose slots hold row 2vi+1's chunks 28-31 (lane
+            // group 8 + (7 ^ (so >> 2))) load row 2vi's rope instead (rope
+            // chunk (c - 28) ^ swz_r for slot c), for line_fix to exchange
+            // with the rope region.  The row offset is the scalar soff; the
+            // descriptor ends at the tile's valid rows (past them: zeros).
+            const int se = F::swz_v(2 * vi), so = se ^ 2;
+            const int nrm = (lkey ^ (16 * se)) + h576;
+            const int exc = rkey512 ^ (16 * ((so & 3) ^ F::swz_r(2 * vi)));
+            voff = lane4 == 8 + (7 ^ (so >> 2)) ? exc : nrm;
+            soff = 2 * vi * kRowBytes;
           } else {
             // rows 2vi (lanes 0-31) and 2vi+1 (lanes 32-63); F::swz_v(2vi+1) = F::swz_v(2vi) ^ 2
             const int row = 2 * vi + keep(v_half);
@@ -552,9 +590,16 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
           dma_lds16(rsrc, lbase + vi * 1024, voff, soff);
         };
         auto dma_r = [&](int ri) {
-          const int row = ri * kRowsPerRope + rope_row_in;
-          const int voff = clamp(row) * kRowBytes + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
-          dma_lds16(rsrc, lbase + (kNIV + ri) * 1024, voff, 0);
+          if constexpr (kLineDma) {
+            // the ninth line of row pairs 8ri .. 8ri+7 (row 2a+1's latent
+            // chunks 28-31, then its rope) into the rope slots of rows 2a
+            // (the latent chunks, for line_fix) and 2a+1
+            dma_lds16(rsrc, lbase + (kNIV + ri) * 1024, l8off, 16 * kRowBytes * ri);
+          } else {
+            const int row = ri * kRowsPerRope + rope_row_in;
+            const int voff = clamp(row) * kRowBytes + kKvRank * (FP8 ? 1 : 2) + 16 * (rope_cpos ^ F::swz_r(row));
+            dma_lds16(rsrc, lbase + (kNIV + ri) * 1024, voff, 0);
+          }
         };
         if (prod_mode) {
           // A wave without rows issues the whole tile; the others none.
@@ -629,6 +674,20 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
         }
       }
     }
+  };
+
+  // The exchange that completes a whole-line tile: lane (a, q) swaps row
+  // 2a+1's latent slot 28+q (which the DMA filled with row 2a's rope) with
+  // row 2a's rope slot q (filled with row 2a+1's latent chunk 28+q).
+  auto line_fix = [&](const char* buf) {
+    const int a = lane >> 2, q = lane & 3;
+    const int x = 1024 * a + 512 + 16 * ((28 + q) ^ F::swz_v(2 * a + 1));
+    const int y = kVRegion + 2 * a * F::kRopePitch + 16 * q;
+    LDS_AS u32x4* px = (LDS_AS u32x4*)(buf + x);
+    LDS_AS u32x4* py = (LDS_AS u32x4*)(buf + y);
+    const u32x4 vx = *px, vy = *py;
+    *px = vy;
+    *py = vx;
   };
 
   // Per-lane LDS read geometry (see the layout note above KvFmt).
@@ -1078,6 +1137,7 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
       }
       if (!wave_has_rows) continue;
       const char* buf = lds[slot0 + k % NBUF];
+      if constexpr (kLineDma) line_fix(buf);
       SBlk sblk;
       qk_tile(buf, qop, qlat, qrope, sblk);
       PVal pvv;
