@@ -373,9 +373,11 @@ __device__ __forceinline__ void run_piece(const SegmentLaunch& p,
   // instructions touch 176 lines for its 144 (a plain DMA stream measured
   // 5.9 TB/s that way, 6.8 TB/s over whole lines).  A lone wave (NW 1) loads
   // whole lines instead and restores the layout with one exchange of 64
-  // chunks per tile (line_fix), before it reads the tile.  (A producer wave
-  // doing the same before the tile's barrier measured 3% slower at 48 heads:
-  // the exchange delays the three computing waves.)
+  // chunks per tile (line_fix), before it reads the tile.  (The four-wave
+  // body's producer wave doing the same measured 3% slower at 48 heads when
+  // it exchanged tile k before the barrier that releases it, and no faster
+  // when it exchanged tile k+1 while the others computed on tile k: there the
+  // waves' own tile work, not the memory path, sets the pace.)
   constexpr bool kLineDma = FP8 && CONTIG && NW == 1;
   const int active_waves = cdiv(min(M - row0, kRowsWG), 16 * RG);
   const bool prod_mode = kProd && active_waves < NW;
