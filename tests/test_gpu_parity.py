@@ -180,6 +180,24 @@ def test_parity_sweep(case):
 
 
 @pytest.mark.parametrize("schedule", ["segments", "balanced"])
+def test_fp8_one_wave_tiles_every_tail_length(schedule):
+    """fp8 at 16 heads over 64-key pages: the one-wave ring loads whole cache
+    lines of 32-row tiles and exchanges 64 chunks per tile.  One request per
+    count of valid rows in its last tile (1..32), at one to three tiles in
+    front of it, so rows past a tile's end (zeros) never reach a result."""
+    lens = [32 * (1 + r % 3) + r for r in range(1, 33)]
+    _print_case(f"fp8 one-wave tail lengths {schedule}")
+    w = mi.make_workload(name="tails", seq_lens=lens, num_heads=16, block_size=64, dtype="fp8_e4m3",
+                         sinks=True, seed=4242)
+    ref_o, ref_l = orc.mla_decode(w)
+    for S in ((0, 2) if schedule == "segments" else (0,)):
+        out, lse = run_decode(w, num_segments=S, schedule=schedule)
+        assert_close(w, out, lse, ref_o, ref_l)
+    out_b, lse_b = run_decode(w, num_segments=0, schedule=schedule, out_dtype=torch.bfloat16)
+    assert_close(w, out_b, lse_b, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("schedule", ["segments", "balanced"])
 def test_planner_choice_and_empty_requests(schedule):
     """num_segments = 0 (the planner's S, or the balanced split) and requests
     of length 0, with sinks."""
