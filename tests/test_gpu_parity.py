@@ -337,6 +337,45 @@ def test_split_many_requests(R, wgs):
     assert_close(w, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_l)
 
 
+PER_JOB = [
+    # (dtype, H, block, lens, qlens, workgroups, sum_seq_lens hint or None for the exact sum)
+    # k workgroups per job (request row chunk) of U units:
+    ("bf16", 16, 64, [1000] * 6, None, 30, None),             # 63 units per job, 5 per job
+    ("fp8_e4m3", 48, 64, [1500] * 5, None, 45, None),         # producer wave: 47 units, 9 per job
+    ("bf16", 16, 64, [700] * 4, [2] * 4, 24, None),           # 2 row chunks per request, records
+    ("fp8_e4m3", 64, 64, [900] * 3, None, 12, None),          # wide fp8 waves: 29 units, 4 per job
+    ("bf16", 128, 128, [800] * 3, None, 18, None),            # wide bf16 waves: 25 units, 6 per job
+    ("bf16", 16, 64, [1000] * 6, None, 6, None),              # one workgroup per job: finished in place
+    ("bf16", 16, 64, [20] * 6, None, 30, None),               # 2 units over 5 workgroups: empty pieces
+    ("bf16", 16, 64, [1000, 900] + [1000] * 4, None, 30, 6000),  # a hint that claims equal lengths
+]
+
+
+@pytest.mark.parametrize("case", PER_JOB, ids=lambda c: f"{c[0]}-H{c[1]}-L{c[3][0]}-wg{c[5]}-hint{c[6]}")
+def test_split_per_job_ranges(case):
+    """Equal jobs (one request's row chunk each) on k workgroups per job, also
+    when k does not divide a job's units: the shares of the whole unit
+    sequence then still end on job boundaries (floor((k j + i) U / k) =
+    j U + floor(i U / k)).  Also one workgroup per job (rows finished in
+    place), jobs of fewer units than workgroups (empty ranges), and a length
+    hint that claims equal lengths when they are not."""
+    import mla_paged_decode_02_amd as m
+    dtype, H, block, lens, qlens, wgs, hint = case
+    _print_case(f"split per-job ranges {case}")
+    w = mi.make_workload(name="perjob", seq_lens=lens, qlens=qlens, num_heads=H, block_size=block, dtype=dtype,
+                         causal=qlens is not None, sinks=True, seed=4700 + H + wgs)
+    ref_o, ref_l = orc.mla_decode(w)
+    d = mi.to_torch(w, "cuda")
+    args = mi.call_args(w, d)
+    if hint is not None:
+        args["sum_seq_lens"] = hint
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out, lse = m.decode(**args, sinks=d["sinks"], schedule="balanced", max_workgroups=wgs, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert_close(w, out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                     ref_o, ref_l)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
 def test_split_long_row_among_short_ones(dtype):
     """One long request among many short ones: the merge's step size follows
